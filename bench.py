@@ -1,0 +1,262 @@
+"""Benchmark: W4A16 decode projections on one MI355X.
+
+A step is one decode token through the projections of a 42-layer,
+2560-hidden transformer (the Gemma-4 E4B shapes of the decode workload):
+per layer q, k, v, o (2560/512/512/2560 <- 2560), fused gate+up
+(20480 <- 2560) and down (2560 <- 10240), each a separate w4a16_matmul at
+M = 1, every layer with its own weights (2.2 GB in total, far beyond the
+256 MB last-level cache, so each call streams its weights from HBM).  The
+step is captured once in a HIP graph and replayed.  The same step at
+M = k+1 in {2, 3, 5} (speculative-verify batches) is reported alongside.
+
+Prints ONE JSON line.  The value is whole-step throughput in algorithmic
+GB/s: packed codes + bf16 scales/biases + bf16 x + bf16 y per call.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synthetic  # noqa: E402
+
+METRIC = "achieved HBM GB/s (% of MI355X peak) for W4A16 qmv M=1 and qmm M=k+1"
+PEAK_GBS = 8000.0
+LAYERS = 42
+
+
+def call_bytes(M: int, N: int, K: int) -> int:
+    """Algorithmic bytes of one product: codes + scales + biases + x + y (bf16)."""
+    return N * K // 2 + N * (K // 64) * 4 + 2 * M * K + 2 * M * N
+
+
+def step_bytes(M: int, layers: int) -> int:
+    return layers * sum(call_bytes(M, *synthetic.PROJECTIONS[p]) for p in synthetic.LAYER_ORDER)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_stack(torch, layers: int):
+    """Per projection: seeded layer-0 weights uploaded, other layers' codes xor-ed on device."""
+    from decode_w4a16_affine_amd import GROUP
+
+    stack = {}
+    host0 = {}
+    for i, p in enumerate(synthetic.LAYER_ORDER):
+        N, K = synthetic.PROJECTIONS[p]
+        w = synthetic.quantized_weights(N, K, seed=0, tag=(i,))
+        host0[p] = w
+        qw0 = torch.from_numpy(w.qw.view(np.int32)).cuda()
+        s0 = torch.from_numpy(w.scales.view(np.int16)).view(torch.bfloat16).cuda()
+        b0 = torch.from_numpy(w.biases.view(np.int16)).view(torch.bfloat16).cuda()
+        qw = torch.empty((layers, N, K // 8), dtype=torch.int32, device="cuda")
+        s = torch.empty((layers, N, K // GROUP), dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(s)
+        for l in range(layers):
+            key = np.array([(0x9E3779B9 * l) & 0xFFFFFFFF], dtype=np.uint32).view(np.int32)[0]
+            qw[l] = qw0 ^ int(key)
+            s[l] = s0
+            b[l] = b0
+        x = synthetic.activations(8, K, seed=0, tag=(100 + i,))
+        xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        y = torch.empty((8, N), dtype=torch.bfloat16, device="cuda")
+        stack[p] = dict(qw=qw, s=s, b=b, x=xd, y=y, N=N, K=K)
+    torch.cuda.synchronize()
+    return stack, host0
+
+
+def make_step(w4, stack, M: int, layers: int, only=None):
+    order = [p for p in synthetic.LAYER_ORDER if only is None or p in only]
+    xs = {p: stack[p]["x"][:M] for p in order}
+    ys = {p: stack[p]["y"][:M] for p in order}
+
+    def step():
+        for l in range(layers):
+            for p in order:
+                d = stack[p]
+                w4.w4a16_matmul(xs[p], d["qw"][l], d["s"][l], d["b"][l], ys[p])
+
+    return step
+
+
+def capture(torch, fn):
+    fn()  # eager warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, steps: int, warmup: int) -> float:
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    # graph replays run on the current stream, where the events are recorded
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def kernel_durations(torch, w4, stack, layers: int, reps: int = 20):
+    """Average duration of each projection's launch, measured with events
+    recorded on the launch stream immediately around single eager launches
+    (layers rotate so every launch is cold)."""
+    out = {}
+    s = torch.cuda.current_stream()
+    for p in synthetic.LAYER_ORDER:
+        d = stack[p]
+        x, y = d["x"][:1], d["y"][:1]
+        times = []
+        for r in range(reps + 3):
+            l = r % layers
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            w4.w4a16_matmul(x, d["qw"][l], d["s"][l], d["b"][l], y, stream=s)
+            e1.record(s)
+            e1.synchronize()
+            if r >= 3:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        out[p] = float(np.median(times))
+    return out
+
+
+def cpu_baseline(host0, seconds: float = 10.0):
+    """The oracle, as it stands, on one host core over layer 0's projections."""
+    import oracle
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    xs = {p: synthetic.activations(1, host0[p].K, seed=0, tag=(100 + i,))
+          for i, p in enumerate(synthetic.LAYER_ORDER)}
+    done_bytes = 0
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        for p in synthetic.LAYER_ORDER:
+            w = host0[p]
+            oracle.qmm(xs[p], w.qw, w.scales, w.biases)
+            done_bytes += call_bytes(1, w.N, w.K)
+            calls += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(done_bytes / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{calls} single-row products over one layer's q,k,v,o,gate_up,down weights "
+                       f"({calls // 6} layer passes, {dt:.1f} s, 1 thread, fp64 accumulation)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the product shards by rows or experts; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_w4a16_affine_amd as w4
+
+    w4.lib()  # fails loudly when the HIP library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L = args.layers
+    log(f"building {L}-layer weight stack")
+    stack, host0 = build_stack(torch, L)
+
+    results = {}
+    Ms = [1] if args.no_verify else [1] + list(synthetic.VERIFY_M)
+    for M in Ms:
+        g = capture(torch, make_step(w4, stack, M, L))
+        steps = args.steps if M == 1 else max(10, args.steps // 2)
+        warm = args.warmup if M == 1 else max(3, args.warmup // 2)
+        ms = time_graph(torch, g, steps, warm)
+        nb = step_bytes(M, L)
+        results[M] = dict(ms=ms, gbs=nb / (ms * 1e-3) / 1e9, bytes=nb, steps=steps, warmup=warm)
+        log(f"M={M}: {ms:.4f} ms/step, {results[M]['gbs']:.1f} GB/s")
+        del g
+
+    # Dominant kernel: per-launch durations, events around single launches.
+    dur = kernel_durations(torch, w4, stack, L)
+    # gate_up runs the wide-matrix kernel; q, k, v, o, down share the K-split one.
+    wide = ["gate_up"]
+    narrow = [p for p in synthetic.LAYER_ORDER if p not in wide]
+    groups = {"wide (gate_up)": wide, "K-split (q,k,v,o,down)": narrow}
+    per_group = {}
+    for name, ps in groups.items():
+        t = sum(dur[p] for p in ps)
+        b = sum(call_bytes(1, *synthetic.PROJECTIONS[p]) for p in ps)
+        per_group[name] = dict(us_total=t, bytes_total=b, launches=len(ps))
+    dom = max(per_group, key=lambda k: per_group[k]["us_total"])
+    pg = per_group[dom]
+    avg_us = pg["us_total"] / pg["launches"]
+    avg_bytes = pg["bytes_total"] / pg["launches"]
+    achieved = avg_bytes / (avg_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_GBS, 4), traffic=None,
+                    kernel=dom, avg_launch_us=round(avg_us, 3), avg_launch_bytes=int(avg_bytes),
+                    per_projection_us={p: round(v, 3) for p, v in dur.items()},
+                    per_projection_gbs={p: round(call_bytes(1, *synthetic.PROJECTIONS[p]) / (v * 1e-6) / 1e9, 1)
+                                        for p, v in dur.items()})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, 1 core)")
+        cpu = cpu_baseline(host0, args.cpu_seconds)
+
+    r1 = results[1]
+    line = {
+        "metric": METRIC,
+        "value": round(r1["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": r1["steps"],
+        "warmup": r1["warmup"],
+        "ms_per_step": round(r1["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode step, M=1: {L} layers x (q,k,v,o 2560/512/512/2560<-2560, "
+                               "gate_up 20480<-2560, down 2560<-10240), W4 group 64, bf16 x/y, "
+                               "one HIP graph per step",
+                   "layers": L, "bytes_per_step": r1["bytes"], "frac_of_peak": round(r1["gbs"] / PEAK_GBS, 4)},
+        "verify": {str(M): dict(gbs=round(r["gbs"], 2), ms_per_step=round(r["ms"], 5),
+                                frac_of_peak=round(r["gbs"] / PEAK_GBS, 4),
+                                cost_vs_m1=round(r["ms"] / r1["ms"], 4))
+                   for M, r in results.items() if M != 1},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+"""Python binding of the W4A16 decode library (libw4a16.so, gfx950).
+
+The functions carry the C-ABI names of include/w4a16.h and only marshal
+arguments: torch tensors become device pointers and the current HIP stream;
+every step of the computation runs in the library's kernels.  If the library
+is not built, importing works but every call raises.
+
+Tensor conventions (all on the same GPU, contiguous):
+  x, scales, biases, bf16 outputs : torch.bfloat16
+  qw                              : torch.int32 (the uint32 words, bit for bit)
+  ids, argmax, rows               : torch.int32
+  fp32 outputs                    : torch.float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+OUT_BF16 = 0
+OUT_F32 = 1
+GROUP = 64
+MAX_M = 8
+
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN",
+          5: "ERR_WORKSPACE", 6: "ERR_HIP"}
+
+EXPORTS = ("w4a16_matmul", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
+           "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_pack", "w4a16_status_str",
+           "w4a16_abi_version")
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_str(status)})")
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+_size = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a16.so; raises if it is not built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.w4a16_matmul.restype = _int
+        L.w4a16_matmul.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]
+        L.w4a16_matmul_id.restype = _int
+        L.w4a16_matmul_id.argtypes = [_vp, _int, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
+                                      _int, _int, _vp]
+        L.w4a16_lmhead_argmax_workspace_bytes.restype = _size
+        L.w4a16_lmhead_argmax_workspace_bytes.argtypes = [_int, _int, _int, _int]
+        L.w4a16_lmhead_argmax.restype = _int
+        L.w4a16_lmhead_argmax.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _size, _int, _int,
+                                          _int, _int, _vp]
+        L.w4a16_dequant.restype = _int
+        L.w4a16_dequant.argtypes = [_vp, _vp, _vp, _vp, _int, _vp, _int, _int, _int, _vp]
+        L.w4a16_pack.restype = _int
+        L.w4a16_pack.argtypes = [_vp, _vp, _int, _int, _vp]
+        L.w4a16_status_str.restype = ctypes.c_char_p
+        L.w4a16_status_str.argtypes = [_int]
+        L.w4a16_abi_version.restype = _int
+        L.w4a16_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _status_str(s: int) -> str:
+    try:
+        return lib().w4a16_status_str(s).decode()
+    except Exception:
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise W4A16Error(status, what)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _out_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return OUT_BF16
+    if t.dtype == torch.float32:
+        return OUT_F32
+    raise TypeError("outputs are torch.bfloat16 or torch.float32")
+
+
+def _dtype(t, want, name):
+    if t.dtype != want:
+        raise TypeError(f"{name} must be {want}, got {t.dtype}")
+
+
+# ---- C-ABI entry points ---------------------------------------------------------
+
+def w4a16_matmul(x, qw, scales, biases, y, group: int = GROUP, stream=None) -> None:
+    """y[M,N] = x[M,K] . W^T  (W = packed qw [N,K/8] with bf16 scales/biases [N,K/64])."""
+    _dtype(x, torch.bfloat16, "x"); _dtype(qw, torch.int32, "qw")
+    M, K = x.shape
+    N = qw.shape[0]
+    _check(lib().w4a16_matmul(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(y), _out_code(y),
+                              M, N, K, group, _stream(stream)), "w4a16_matmul")
+
+
+def w4a16_matmul_id(x, qw, scales, biases, ids, y, x_per_slot: bool = False, group: int = GROUP,
+                    stream=None) -> None:
+    """y[M,top_k,N]: slot (m,j) uses expert ids[m,j] of the stack qw [E,N,K/8]."""
+    _dtype(x, torch.bfloat16, "x"); _dtype(qw, torch.int32, "qw"); _dtype(ids, torch.int32, "ids")
+    M, top_k = ids.shape
+    E, N = qw.shape[0], qw.shape[1]
+    K = x.shape[-1]
+    _check(lib().w4a16_matmul_id(_ptr(x), int(bool(x_per_slot)), _ptr(qw), _ptr(scales), _ptr(biases),
+                                 _ptr(ids), _ptr(y), _out_code(y), M, top_k, E, N, K, group,
+                                 _stream(stream)), "w4a16_matmul_id")
+
+
+def w4a16_lmhead_argmax_workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
+    return int(lib().w4a16_lmhead_argmax_workspace_bytes(M, N, K, group))
+
+
+def w4a16_lmhead_argmax(x, qw, scales, biases, logits, argmax, workspace, group: int = GROUP,
+                        stream=None, out_dtype=None) -> None:
+    """argmax[M] (int32) of x . W^T, optional logits [M,N]; workspace: a uint8 device tensor."""
+    _dtype(x, torch.bfloat16, "x"); _dtype(qw, torch.int32, "qw"); _dtype(argmax, torch.int32, "argmax")
+    M, K = x.shape
+    N = qw.shape[0]
+    code = _out_code(logits) if logits is not None else (OUT_BF16 if out_dtype is None else out_dtype)
+    _check(lib().w4a16_lmhead_argmax(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(logits), code,
+                                     _ptr(argmax), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     M, N, K, group, _stream(stream)), "w4a16_lmhead_argmax")
+
+
+def w4a16_dequant(qw, scales, biases, out, rows=None, group: int = GROUP, stream=None) -> None:
+    """out[R,K] (fp32) = dequantized rows (rows=None: all N rows)."""
+    _dtype(qw, torch.int32, "qw"); _dtype(out, torch.float32, "out")
+    N = qw.shape[0]
+    K = qw.shape[1] * 8
+    R = rows.numel() if rows is not None else N
+    _check(lib().w4a16_dequant(_ptr(qw), _ptr(scales), _ptr(biases), _ptr(rows), R, _ptr(out), N, K, group,
+                               _stream(stream)), "w4a16_dequant")
+
+
+def w4a16_pack(codes, qw, stream=None) -> None:
+    """codes uint8 [N,K] -> qw int32 [N,K/8] (first code in the lowest nibble)."""
+    _dtype(codes, torch.uint8, "codes"); _dtype(qw, torch.int32, "qw")
+    N, K = codes.shape
+    _check(lib().w4a16_pack(_ptr(codes), _ptr(qw), N, K, _stream(stream)), "w4a16_pack")
+
+
+def w4a16_status_str(status: int) -> str:
+    return _status_str(status)
+
+
+def w4a16_abi_version() -> int:
+    return int(lib().w4a16_abi_version())
+
+
+# ---- allocating conveniences (torch allocates; the library computes) ------------
+
+def matmul(x, qw, scales, biases, out_dtype=torch.bfloat16, stream=None):
+    y = torch.empty((x.shape[0], qw.shape[0]), dtype=out_dtype, device=x.device)
+    w4a16_matmul(x, qw, scales, biases, y, stream=stream)
+    return y
+
+
+def matmul_id(x, qw, scales, biases, ids, x_per_slot=False, out_dtype=torch.bfloat16, stream=None):
+    y = torch.empty((ids.shape[0], ids.shape[1], qw.shape[1]), dtype=out_dtype, device=x.device)
+    w4a16_matmul_id(x, qw, scales, biases, ids, y, x_per_slot=x_per_slot, stream=stream)
+    return y
+
+
+def lmhead_argmax(x, qw, scales, biases, want_logits=True, out_dtype=torch.bfloat16, stream=None):
+    M, K = x.shape
+    N = qw.shape[0]
+    ws = torch.empty(max(1, w4a16_lmhead_argmax_workspace_bytes(M, N, K)), dtype=torch.uint8, device=x.device)
+    am = torch.empty(M, dtype=torch.int32, device=x.device)
+    logits = torch.empty((M, N), dtype=out_dtype, device=x.device) if want_logits else None
+    w4a16_lmhead_argmax(x, qw, scales, biases, logits, am, ws, stream=stream,
+                        out_dtype=OUT_F32 if out_dtype == torch.float32 else OUT_BF16)
+    return am, logits
+
+
+def dequant(qw, scales, biases, rows=None, stream=None):
+    R = rows.numel() if rows is not None else qw.shape[0]
+    out = torch.empty((R, qw.shape[1] * 8), dtype=torch.float32, device=qw.device)
+    w4a16_dequant(qw, scales, biases, out, rows=rows, stream=stream)
+    return out
+
+
+def pack(codes, stream=None):
+    qw = torch.empty((codes.shape[0], codes.shape[1] // 8), dtype=torch.int32, device=codes.device)
+    w4a16_pack(codes, qw, stream=stream)
+    return qw

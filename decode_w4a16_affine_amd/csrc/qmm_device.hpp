@@ -1,0 +1,310 @@
+// Device code of the W4A16 group-affine decode product for gfx950 (CDNA4).
+//
+// One per-row code body serves every entry point (dense, routed, LM head), so
+// a row's arithmetic never depends on how many activation rows share the call.
+//
+// Work decomposition (wave64):
+//   * A 16-byte load holds 32 consecutive codes of one row: half of a 64-code
+//     quantization group, so a load never straddles two groups.
+//   * 16 consecutive lanes ("a row group") stream one row: lane L reads the
+//     16-byte chunks c = L, L + LPR, L + 2*LPR, ... of the row, where LPR is 16
+//     (one row group per row) or 64 (the four waves of a block share a row:
+//     K-split for narrow matrices).  A wave holds four row groups.
+//   * Each lane streams R rows at once so one activation fetch from LDS serves
+//     R rows.  Activations are staged once per block into LDS as fp32.
+//   * Dequantization is literal: w = fma(s, q, b) in fp32 for every weight, with
+//     the code fed to v_fma_mix_f32 as an fp16 subnormal (bits q = value
+//     q * 2^-24, or 16q * 2^-24 for the odd nibble of a byte) and the scale
+//     pre-multiplied by 2^24 (resp. 2^20).  Both factors are powers of two, so
+//     s' * q' equals s * q exactly and the single rounding of the fma equals
+//     that of fma(s, q, b).  Scales with |s| >= 2^100 (where s * 2^24 could
+//     overflow) take a plain fma path instead, chosen per chunk for the wave.
+//   * Products accumulate with fp32 fma in ascending k per lane; lanes combine
+//     through a fixed DPP tree, then (K-split) across waves in wave order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4k {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRowLanes = 16;
+constexpr int kSlots = kWave / kRowLanes;      // row groups per wave
+constexpr int kMaxM = 8;
+constexpr int kLdsXFloats = 15360;             // activation staging budget: 60 KiB per block
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// fp32 -> bf16, IEEE-754 round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Eight weights of one packed word, fast path.  s24 = s * 2^24, s20 = s * 2^20.
+__device__ __forceinline__ void dequant8_fast(uint32_t w, float s24, float s20, float b, float (&o)[8]) {
+  const f16x2 p0 = __builtin_bit_cast(f16x2, w & 0x000F000Fu);          // codes 0, 4
+  const f16x2 p1 = __builtin_bit_cast(f16x2, w & 0x00F000F0u);          // codes 1, 5 (x16)
+  const uint32_t w8 = w >> 8;
+  const f16x2 p2 = __builtin_bit_cast(f16x2, w8 & 0x000F000Fu);         // codes 2, 6
+  const f16x2 p3 = __builtin_bit_cast(f16x2, w8 & 0x00F000F0u);         // codes 3, 7 (x16)
+  o[0] = __builtin_fmaf(s24, (float)p0.x, b);
+  o[1] = __builtin_fmaf(s20, (float)p1.x, b);
+  o[2] = __builtin_fmaf(s24, (float)p2.x, b);
+  o[3] = __builtin_fmaf(s20, (float)p3.x, b);
+  o[4] = __builtin_fmaf(s24, (float)p0.y, b);
+  o[5] = __builtin_fmaf(s20, (float)p1.y, b);
+  o[6] = __builtin_fmaf(s24, (float)p2.y, b);
+  o[7] = __builtin_fmaf(s20, (float)p3.y, b);
+}
+
+// Same eight weights, plain conversion (any finite or non-finite scale).
+__device__ __forceinline__ void dequant8_plain(uint32_t w, float s, float b, float (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = __builtin_fmaf(s, (float)((w >> (4 * i)) & 0xFu), b);
+}
+
+__device__ __forceinline__ bool needs_plain(float s) { return !(__builtin_fabsf(s) < 0x1p100f); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane receives the same value
+// (fp32 addition is commutative, and the tree is fixed).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);   // row_half_mirror
+  v += dpp<0x140>(v);   // row_mirror
+  return v;
+}
+
+// Orderable key of (value, index) for an argmax: larger key = larger value,
+// then lower index.  -0 counts as +0; NaN ranks above every number.
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t n) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
+    u = 0xFFFFFFFFu;
+  } else {
+    if (u == 0x80000000u) u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - n);
+}
+
+template <int M>
+struct XRows {
+  const uint16_t* p[M];
+};
+
+// Stage x[m][k0 .. k0+klen) into LDS as fp32.  Layout (float4 units):
+// xs[(m * 8 + piece) * cseg + c] holds k = k0 + 32c + 4*piece .. +3, so lanes
+// reading consecutive chunks of one piece touch consecutive 16-byte words.
+template <int M>
+__device__ __forceinline__ void stage_x(float4* xs, const XRows<M>& xr, int k0, int klen) {
+  const int cseg = klen >> 5;
+  const int pairs = klen >> 1;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(xr.p[m] + k0);
+    for (int j = threadIdx.x; j < pairs; j += kThreads) {
+      const uint32_t v = src[j];
+      const int kk = 2 * j;
+      const int c = kk >> 5, piece = (kk >> 2) & 7, e = kk & 3;
+      float2* dst = reinterpret_cast<float2*>(reinterpret_cast<float*>(xs + (m * 8 + piece) * cseg + c) + e);
+      *dst = make_float2(bf16_lo(v), bf16_hi(v));
+    }
+  }
+}
+
+// Weights of U chunks x R rows for one lane, in registers.
+template <int U, int R>
+struct Batch {
+  uint4 w[U][R];
+  uint32_t s[U][R];
+  uint32_t b[U][R];
+};
+
+struct RowSrc {
+  const uint32_t* __restrict__ qw;
+  const uint16_t* __restrict__ scales;
+  const uint16_t* __restrict__ biases;
+  int N;      // rows in this matrix
+  int K;
+};
+
+template <int U, int R, int LPR>
+__device__ __forceinline__ void load_batch(Batch<U, R>& bt, const RowSrc& src, int row_first, int cb, int cseg,
+                                           int cbase, int L) {
+  const size_t wpr = (size_t)(src.K >> 3);
+  const int gpr = src.K >> 6;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = cb + u * LPR + L;
+    const int cg = cbase + c;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = row_first + r;
+      if (c < cseg && n < src.N) {
+        bt.w[u][r] = *reinterpret_cast<const uint4*>(src.qw + (size_t)n * wpr + (size_t)cg * 4);
+        bt.s[u][r] = src.scales[(size_t)n * gpr + (cg >> 1)];
+        bt.b[u][r] = src.biases[(size_t)n * gpr + (cg >> 1)];
+      } else {
+        bt.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
+        bt.s[u][r] = 0u;
+        bt.b[u][r] = 0u;
+      }
+    }
+  }
+}
+
+template <int M, int R, bool FAST>
+__device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R], const float (&s)[R],
+                                          const float (&b)[R], const float4* xc, int cseg) {
+  float s24[R], s20[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    s24[r] = s[r] * 0x1p24f;
+    s20[r] = s[r] * 0x1p20f;
+  }
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    float xv[M][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float4 lo = xc[(m * 8 + 2 * wd) * cseg];
+      const float4 hi = xc[(m * 8 + 2 * wd + 1) * cseg];
+      xv[m][0] = lo.x; xv[m][1] = lo.y; xv[m][2] = lo.z; xv[m][3] = lo.w;
+      xv[m][4] = hi.x; xv[m][5] = hi.y; xv[m][6] = hi.z; xv[m][7] = hi.w;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t word = wd == 0 ? w[r].x : wd == 1 ? w[r].y : wd == 2 ? w[r].z : w[r].w;
+      float q[8];
+      if (FAST)
+        dequant8_fast(word, s24[r], s20[r], b[r], q);
+      else
+        dequant8_plain(word, s[r], b[r], q);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[r][m] = __builtin_fmaf(xv[m][i], q[i], acc[r][m]);
+      }
+    }
+  }
+}
+
+template <int M, int U, int R, int LPR>
+__device__ __forceinline__ void compute_batch(float (&acc)[R][M], const Batch<U, R>& bt, const float4* xs, int cb,
+                                              int cseg, int L) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = cb + u * LPR + L;
+    if (c < cseg) {
+      float s[R], b[R];
+      bool plain = false;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        s[r] = __uint_as_float(bt.s[u][r] << 16);
+        b[r] = __uint_as_float(bt.b[u][r] << 16);
+        plain |= needs_plain(s[r]);
+      }
+      if (__any(plain))
+        chunk_fma<M, R, false>(acc, bt.w[u], s, b, xs + c, cseg);
+      else
+        chunk_fma<M, R, true>(acc, bt.w[u], s, b, xs + c, cseg);
+    }
+  }
+}
+
+// Full-row sums for the R rows of this lane's row group.
+// KSPLIT == 1: on return every lane of the row group holds the sums.
+// KSPLIT == 4: the four waves of the block share the rows; on return every
+//              lane of every wave holds the sums (combined in wave order).
+// Must be called by all threads of the block (it synchronizes).
+template <int M, int R, int U, int KSPLIT>
+__device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src, int kseg,
+                                           int row_first, float4* xs, float* red) {
+  constexpr int LPR = kRowLanes * KSPLIT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int t = lane & (kRowLanes - 1);
+  const int slot = lane / kRowLanes;
+  const int L = KSPLIT == 1 ? t : wave * kRowLanes + t;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+  const int K = src.K;
+  for (int k0 = 0; k0 < K; k0 += kseg) {
+    const int klen = min(kseg, K - k0);
+    const int cseg = klen >> 5;
+    const int cbase = k0 >> 5;
+    const int step = LPR * U;
+    const int nb = (cseg + step - 1) / step;
+    Batch<U, R> A, B;
+    // The first weights of the segment are requested before the activations
+    // are staged, so the two latencies overlap.
+    load_batch<U, R, LPR>(A, src, row_first, 0, cseg, cbase, L);
+    __syncthreads();  // every wave is done with the previous contents of xs
+    stage_x<M>(xs, xr, k0, klen);
+    __syncthreads();
+    for (int ib = 0; ib < nb; ib += 2) {
+      if (ib + 1 < nb) load_batch<U, R, LPR>(B, src, row_first, (ib + 1) * step, cseg, cbase, L);
+      compute_batch<M, U, R, LPR>(acc, A, xs, ib * step, cseg, L);
+      if (ib + 1 < nb) {
+        if (ib + 2 < nb) load_batch<U, R, LPR>(A, src, row_first, (ib + 2) * step, cseg, cbase, L);
+        compute_batch<M, U, R, LPR>(acc, B, xs, (ib + 1) * step, cseg, L);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = row16_sum(acc[r][m]);
+
+  if (KSPLIT > 1) {
+    if (t == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) red[((wave * kSlots + slot) * R + r) * M + m] = acc[r][m];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float v = red[((0 * kSlots + slot) * R + r) * M + m];
+#pragma unroll
+        for (int w = 1; w < KSPLIT; ++w) v += red[((w * kSlots + slot) * R + r) * M + m];
+        acc[r][m] = v;
+      }
+  }
+}
+
+// Rows handled by a block and the first row of this thread's row group.
+template <int R, int KSPLIT>
+struct RowMap {
+  static constexpr int kRowsPerBlock = (KSPLIT == 1 ? kWaves * kSlots : kSlots) * R;
+  __device__ static int first_row(int block_row0) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int slot = lane / kRowLanes;
+    const int group = KSPLIT == 1 ? wave * kSlots + slot : slot;
+    return block_row0 + group * R;
+  }
+};
+
+}  // namespace w4k

@@ -1,0 +1,507 @@
+// C ABI and kernels of the W4A16 group-affine decode library (gfx950).
+// The operation, layouts and error behaviour are specified in include/w4a16.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "qmm_device.hpp"
+#include "w4a16.h"
+
+using namespace w4k;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Schedules.  KSPLIT (how many row groups share one row) fixes a row's
+// arithmetic and is a function of (N, K) only; R (rows per lane) and U
+// (chunks per lane per batch) only change how much is in flight and may
+// depend on M.
+// ---------------------------------------------------------------------------
+
+constexpr int kNarrowN = 4096;
+
+int ksplit_for(int N, int /*K*/) { return N <= kNarrowN ? 4 : 1; }
+
+constexpr int cfg_R(int M, int ksplit) { return ksplit == 4 ? 2 : (M <= 2 ? 2 : 4); }
+constexpr int cfg_U(int M, int ksplit) { return ksplit == 4 ? 1 : (M <= 2 ? 2 : 1); }
+
+// Activation segment length: a multiple of the chunk-interleave period
+// (32 codes x 16 x KSPLIT) so segmenting never changes a lane's chunk order.
+int kseg_for(int M, int K, int ksplit) {
+  const int unit = 32 * kRowLanes * ksplit;
+  int cap = (kLdsXFloats / M) / unit * unit;
+  if (cap < unit) cap = unit;
+  return K <= cap ? K : cap;
+}
+
+int rows_per_block(int M, int ksplit) {
+  const int R = ksplit == 4 ? cfg_R(M, 4) : cfg_R(M, 1);
+  return (ksplit == 1 ? kWaves * kSlots : kSlots) * R;
+}
+
+// ---------------------------------------------------------------------------
+// Kernels
+// ---------------------------------------------------------------------------
+
+template <int M, int R, int KSPLIT>
+__device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first, int N, void* y,
+                                         const size_t (&yoff)[M], bool out_f32) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int t = lane & (kRowLanes - 1);
+  if (KSPLIT > 1 && wave != 0) return;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int n = row_first + r;
+      if (((r * M + m) & (kRowLanes - 1)) == t && n < N) {
+        if (out_f32)
+          reinterpret_cast<float*>(y)[yoff[m] + n] = acc[r][m];
+        else
+          reinterpret_cast<uint16_t*>(y)[yoff[m] + n] = (uint16_t)f32_to_bf16(acc[r][m]);
+      }
+    }
+}
+
+template <int M, int R, int U, int KSPLIT>
+__global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __restrict__ x,
+                                                             const uint32_t* __restrict__ qw,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ biases, void* __restrict__ y,
+                                                             int out_f32, int N, int K, int kseg) {
+  extern __shared__ float4 xs[];
+  __shared__ float red[kWaves * kSlots * R * M];
+  using RM = RowMap<R, KSPLIT>;
+  XRows<M> xr;
+  size_t yoff[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    xr.p[m] = x + (size_t)m * K;
+    yoff[m] = (size_t)m * N;
+  }
+  const RowSrc src{qw, scales, biases, N, K};
+  const int row_first = RM::first_row(blockIdx.x * RM::kRowsPerBlock);
+  float acc[R][M];
+  block_rows<M, R, U, KSPLIT>(acc, xr, src, kseg, row_first, xs, red);
+  store_to<M, R, KSPLIT>(acc, row_first, N, y, yoff, out_f32 != 0);
+}
+
+template <int M, int R, int U, int KSPLIT>
+__global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __restrict__ x,
+                                                              const uint32_t* __restrict__ qw,
+                                                              const uint16_t* __restrict__ scales,
+                                                              const uint16_t* __restrict__ biases,
+                                                              void* __restrict__ logits, int out_f32,
+                                                              uint64_t* __restrict__ partial, int N, int K, int kseg) {
+  extern __shared__ float4 xs[];
+  __shared__ float red[kWaves * kSlots * R * M];
+  __shared__ uint64_t keys[kWaves * kSlots][M];
+  using RM = RowMap<R, KSPLIT>;
+  XRows<M> xr;
+  size_t yoff[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    xr.p[m] = x + (size_t)m * K;
+    yoff[m] = (size_t)m * N;
+  }
+  const RowSrc src{qw, scales, biases, N, K};
+  const int row_first = RM::first_row(blockIdx.x * RM::kRowsPerBlock);
+  float acc[R][M];
+  block_rows<M, R, U, KSPLIT>(acc, xr, src, kseg, row_first, xs, red);
+  if (logits) store_to<M, R, KSPLIT>(acc, row_first, N, logits, yoff, out_f32 != 0);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int t = lane & (kRowLanes - 1);
+  const int slot = lane / kRowLanes;
+  if (t == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int n = row_first + r;
+        if (n < N) {
+          const uint64_t k = argmax_key(acc[r][m], (uint32_t)n);
+          best = k > best ? k : best;
+        }
+      }
+      keys[wave * kSlots + slot][m] = (KSPLIT == 1 || wave == 0) ? best : 0;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < M) {
+    uint64_t best = 0;
+    for (int i = 0; i < kWaves * kSlots; ++i) {
+      const uint64_t k = keys[i][threadIdx.x];
+      best = k > best ? k : best;
+    }
+    partial[(size_t)blockIdx.x * M + threadIdx.x] = best;
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __restrict__ partial, int nblocks, int M,
+                                                              int32_t* __restrict__ argmax) {
+  __shared__ uint64_t s[256];
+  const int m = blockIdx.x;
+  uint64_t best = 0;
+  for (int i = threadIdx.x; i < nblocks; i += 256) {
+    const uint64_t k = partial[(size_t)i * M + m];
+    best = k > best ? k : best;
+  }
+  s[threadIdx.x] = best;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) s[threadIdx.x] = s[threadIdx.x + w] > s[threadIdx.x] ? s[threadIdx.x + w] : s[threadIdx.x];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) argmax[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)(s[0] & 0xFFFFFFFFull));
+}
+
+// One pass of the routed product: C slots routed to one expert.
+template <int C, int R, int U, int KSPLIT>
+__device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, int x_per_slot, int top_k,
+                                            const RowSrc& src, int kseg, int row_first, void* y, bool out_f32,
+                                            float4* xs, float* red) {
+  XRows<C> xr;
+  size_t yoff[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int sl = list[i];
+    xr.p[i] = x + (size_t)(x_per_slot ? sl : sl / top_k) * src.K;
+    yoff[i] = (size_t)sl * src.N;
+  }
+  float acc[R][C];
+  block_rows<C, R, U, KSPLIT>(acc, xr, src, kseg, row_first, xs, red);
+  store_to<C, R, KSPLIT>(acc, row_first, src.N, y, yoff, out_f32);
+}
+
+template <int MB, int R, int U, int KSPLIT>
+__global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __restrict__ x, int x_per_slot,
+                                                              const uint32_t* __restrict__ qw,
+                                                              const uint16_t* __restrict__ scales,
+                                                              const uint16_t* __restrict__ biases,
+                                                              const int32_t* __restrict__ ids, void* __restrict__ y,
+                                                              int out_f32, int M, int top_k, int E, int N, int K,
+                                                              int kseg, int tiles) {
+  extern __shared__ float4 xs[];
+  __shared__ float red[kWaves * kSlots * R * MB];
+  using RM = RowMap<R, KSPLIT>;
+  const int nslots = M * top_k;
+  const int slot = blockIdx.x / tiles;
+  const int tile = blockIdx.x - slot * tiles;
+  const int block_row0 = tile * RM::kRowsPerBlock;
+  const int e = ids[slot];
+  if (e < 0 || e >= E) {
+    // precondition violation: make the slot's output unmistakable
+    for (int i = threadIdx.x; i < RM::kRowsPerBlock; i += kThreads) {
+      const int n = block_row0 + i;
+      if (n < N) {
+        if (out_f32)
+          reinterpret_cast<float*>(y)[(size_t)slot * N + n] = __builtin_nanf("");
+        else
+          reinterpret_cast<uint16_t*>(y)[(size_t)slot * N + n] = 0x7FC0u;
+      }
+    }
+    return;
+  }
+  for (int j = 0; j < slot; ++j)
+    if (ids[j] == e) return;  // an earlier slot streams this expert
+  const size_t wpr = (size_t)(K >> 3);
+  const size_t gpr = (size_t)(K >> 6);
+  const RowSrc src{qw + (size_t)e * N * wpr, scales + (size_t)e * N * gpr, biases + (size_t)e * N * gpr, N, K};
+  const int row_first = RM::first_row(block_row0);
+  int j = slot;
+  while (j < nslots) {
+    int list[MB];
+    int cnt = 0;
+    for (; j < nslots && cnt < MB; ++j)
+      if (ids[j] == e) list[cnt++] = j;
+    if (cnt == 0) break;
+    switch (cnt) {
+      case 1: routed_pass<1, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      case 2: if constexpr (MB >= 2) routed_pass<2, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      case 3: if constexpr (MB >= 3) routed_pass<3, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      case 4: if constexpr (MB >= 4) routed_pass<4, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      case 5: if constexpr (MB >= 5) routed_pass<5, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      case 6: if constexpr (MB >= 6) routed_pass<6, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      case 7: if constexpr (MB >= 7) routed_pass<7, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      default: if constexpr (MB >= 8) routed_pass<8, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void dequant_rows_kernel(const uint32_t* __restrict__ qw,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint16_t* __restrict__ biases,
+                                                           const int32_t* __restrict__ rows, int R,
+                                                           float* __restrict__ out, int N, int K) {
+  const size_t wpr = (size_t)(K >> 3);
+  const size_t gpr = (size_t)(K >> 6);
+  const size_t total = (size_t)R * wpr;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / wpr;
+    const size_t j = i - r * wpr;
+    const int n = rows ? rows[r] : (int)r;
+    float o[8];
+    if (n < 0 || n >= N) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = __builtin_nanf("");
+    } else {
+      const uint32_t w = qw[(size_t)n * wpr + j];
+      const float s = __uint_as_float((uint32_t)scales[(size_t)n * gpr + (j >> 3)] << 16);
+      const float b = __uint_as_float((uint32_t)biases[(size_t)n * gpr + (j >> 3)] << 16);
+      if (needs_plain(s))
+        dequant8_plain(w, s, b, o);
+      else
+        dequant8_fast(w, s * 0x1p24f, s * 0x1p20f, b, o);
+    }
+    float4* dst = reinterpret_cast<float4*>(out + r * (size_t)K + 8 * j);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, uint32_t* __restrict__ qw,
+                                                   size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x) {
+    const uint8_t* c = codes + 8 * i;
+    uint32_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w |= ((uint32_t)c[q] & 0xFu) << (4 * q);
+    qw[i] = w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+w4a16_status_t launched(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+
+w4a16_status_t check_shape(int M, int N, int K, int group, int out_dtype) {
+  if (group != 64) return W4A16_ERR_UNSUPPORTED;
+  if (out_dtype != W4A16_OUT_BF16 && out_dtype != W4A16_OUT_F32) return W4A16_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0) return W4A16_ERR_SHAPE;
+  if (M > W4A16_MAX_M) return W4A16_ERR_UNSUPPORTED;
+  if (K < 64 || K % 64 != 0) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+w4a16_status_t check_weights(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
+                             const void* y, int out_dtype) {
+  if (!x || !qw || !scales || !biases || !y) return W4A16_ERR_NULL;
+  if (!aligned(qw, 16) || !aligned(x, 4) || !aligned(scales, 2) || !aligned(biases, 2) ||
+      !aligned(y, out_dtype == W4A16_OUT_F32 ? 4 : 2))
+    return W4A16_ERR_ALIGN;
+  return W4A16_OK;
+}
+
+template <int M, int KSPLIT>
+hipError_t launch_dense(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
+                        int out_f32, int N, int K, hipStream_t st) {
+  constexpr int R = cfg_R(M, KSPLIT), U = cfg_U(M, KSPLIT);
+  using RM = RowMap<R, KSPLIT>;
+  const int kseg = kseg_for(M, K, KSPLIT);
+  const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
+  const size_t lds = (size_t)M * kseg * sizeof(float);
+  hipLaunchKernelGGL((qmm_dense_kernel<M, R, U, KSPLIT>), dim3(blocks), dim3(kThreads), lds, st, x, qw, s, b, y,
+                     out_f32, N, K, kseg);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t dense_by_split(int ksplit, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                          void* y, int out_f32, int N, int K, hipStream_t st) {
+  return ksplit == 4 ? launch_dense<M, 4>(x, qw, s, b, y, out_f32, N, K, st)
+                     : launch_dense<M, 1>(x, qw, s, b, y, out_f32, N, K, st);
+}
+
+template <int M, int KSPLIT>
+hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* logits,
+                         int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
+  constexpr int R = cfg_R(M, KSPLIT), U = cfg_U(M, KSPLIT);
+  using RM = RowMap<R, KSPLIT>;
+  const int kseg = kseg_for(M, K, KSPLIT);
+  const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
+  *nblocks = blocks;
+  const size_t lds = (size_t)M * kseg * sizeof(float);
+  hipLaunchKernelGGL((qmm_lmhead_kernel<M, R, U, KSPLIT>), dim3(blocks), dim3(kThreads), lds, st, x, qw, s, b, logits,
+                     out_f32, partial, N, K, kseg);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t lmhead_by_split(int ksplit, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                           void* logits, int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
+  return ksplit == 4 ? launch_lmhead<M, 4>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks)
+                     : launch_lmhead<M, 1>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks);
+}
+
+// Routed kernels: MB = most slots one expert is processed with per pass.
+template <int MB, int KSPLIT>
+hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                         const int32_t* ids, void* y, int out_f32, int M, int top_k, int E, int N, int K,
+                         hipStream_t st) {
+  constexpr int R = cfg_R(MB, KSPLIT), U = cfg_U(MB, KSPLIT);
+  using RM = RowMap<R, KSPLIT>;
+  const int kseg = kseg_for(MB, K, KSPLIT);
+  const int tiles = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
+  const size_t blocks = (size_t)tiles * M * top_k;
+  if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  const size_t lds = (size_t)MB * kseg * sizeof(float);
+  hipLaunchKernelGGL((qmm_routed_kernel<MB, R, U, KSPLIT>), dim3((unsigned)blocks), dim3(kThreads), lds, st, x,
+                     x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, kseg, tiles);
+  return hipGetLastError();
+}
+
+template <int MB>
+hipError_t routed_by_split(int ksplit, const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* s,
+                           const uint16_t* b, const int32_t* ids, void* y, int out_f32, int M, int top_k, int E, int N,
+                           int K, hipStream_t st) {
+  return ksplit == 4 ? launch_routed<MB, 4>(x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, st)
+                     : launch_routed<MB, 1>(x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, st);
+}
+
+int lmhead_blocks(int M, int N, int K) {
+  const int rpb = rows_per_block(M, ksplit_for(N, K));
+  return (N + rpb - 1) / rpb;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_status_str(w4a16_status_t s) {
+  switch (s) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_NULL: return "a required pointer is NULL";
+    case W4A16_ERR_SHAPE: return "invalid shape (K must be a positive multiple of 64; sizes non-negative)";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported (group must be 64, M at most 8, out_dtype bf16 or f32)";
+    case W4A16_ERR_ALIGN: return "pointer misaligned";
+    case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
+    case W4A16_ERR_HIP: return "HIP runtime rejected the launch";
+  }
+  return "unknown status";
+}
+
+w4a16_status_t w4a16_matmul(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
+                            void* y, int out_dtype, int M, int N, int K, int group, void* stream) {
+  w4a16_status_t st = check_shape(M, N, K, group, out_dtype);
+  if (st != W4A16_OK) return st;
+  if (M == 0 || N == 0) return W4A16_OK;
+  st = check_weights(x, qw, scales, biases, y, out_dtype);
+  if (st != W4A16_OK) return st;
+  const int f32 = out_dtype == W4A16_OUT_F32;
+  const int ks = ksplit_for(N, K);
+  hipStream_t s = (hipStream_t)stream;
+  switch (M) {
+    case 1: return launched(dense_by_split<1>(ks, x, qw, scales, biases, y, f32, N, K, s));
+    case 2: return launched(dense_by_split<2>(ks, x, qw, scales, biases, y, f32, N, K, s));
+    case 3: return launched(dense_by_split<3>(ks, x, qw, scales, biases, y, f32, N, K, s));
+    case 4: return launched(dense_by_split<4>(ks, x, qw, scales, biases, y, f32, N, K, s));
+    case 5: return launched(dense_by_split<5>(ks, x, qw, scales, biases, y, f32, N, K, s));
+    case 6: return launched(dense_by_split<6>(ks, x, qw, scales, biases, y, f32, N, K, s));
+    case 7: return launched(dense_by_split<7>(ks, x, qw, scales, biases, y, f32, N, K, s));
+    default: return launched(dense_by_split<8>(ks, x, qw, scales, biases, y, f32, N, K, s));
+  }
+}
+
+w4a16_status_t w4a16_matmul_id(const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* scales,
+                               const uint16_t* biases, const int32_t* ids, void* y, int out_dtype, int M, int top_k,
+                               int E, int N, int K, int group, void* stream) {
+  w4a16_status_t st = check_shape(M, N, K, group, out_dtype);
+  if (st != W4A16_OK) return st;
+  if (top_k < 1 || top_k > 64 || E < 1) return W4A16_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A16_OK;
+  st = check_weights(x, qw, scales, biases, y, out_dtype);
+  if (st != W4A16_OK) return st;
+  if (!ids) return W4A16_ERR_NULL;
+  if (!aligned(ids, 4)) return W4A16_ERR_ALIGN;
+  const int f32 = out_dtype == W4A16_OUT_F32;
+  const int ks = ksplit_for(N, K);
+  hipStream_t s = (hipStream_t)stream;
+  // Without duplicate ids in a token, an expert serves at most M slots.
+  if (M == 1) return launched(routed_by_split<1>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
+  if (M == 2) return launched(routed_by_split<2>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
+  if (M <= 4) return launched(routed_by_split<4>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
+  return launched(routed_by_split<8>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
+}
+
+size_t w4a16_lmhead_argmax_workspace_bytes(int M, int N, int K, int group) {
+  if (check_shape(M, N, K, group, W4A16_OUT_BF16) != W4A16_OK || M == 0 || N == 0) return 0;
+  return (size_t)lmhead_blocks(M, N, K) * (size_t)M * sizeof(uint64_t);
+}
+
+w4a16_status_t w4a16_lmhead_argmax(const uint16_t* x, const uint32_t* qw, const uint16_t* scales,
+                                   const uint16_t* biases, void* logits, int out_dtype, int32_t* argmax,
+                                   void* workspace, size_t workspace_bytes, int M, int N, int K, int group,
+                                   void* stream) {
+  w4a16_status_t st = check_shape(M, N, K, group, out_dtype);
+  if (st != W4A16_OK) return st;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (!x || !qw || !scales || !biases || !argmax) return W4A16_ERR_NULL;
+  if (!aligned(qw, 16) || !aligned(x, 4) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(argmax, 4) ||
+      (logits && !aligned(logits, out_dtype == W4A16_OUT_F32 ? 4 : 2)))
+    return W4A16_ERR_ALIGN;
+  const size_t need = w4a16_lmhead_argmax_workspace_bytes(M, N, K, group);
+  if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return W4A16_ERR_ALIGN;
+  const int f32 = out_dtype == W4A16_OUT_F32;
+  const int ks = ksplit_for(N, K);
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* partial = reinterpret_cast<uint64_t*>(workspace);
+  int nb = 0;
+  hipError_t e;
+  switch (M) {
+    case 1: e = lmhead_by_split<1>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+    case 2: e = lmhead_by_split<2>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+    case 3: e = lmhead_by_split<3>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+    case 4: e = lmhead_by_split<4>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+    case 5: e = lmhead_by_split<5>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+    case 6: e = lmhead_by_split<6>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+    case 7: e = lmhead_by_split<7>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+    default: e = lmhead_by_split<8>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
+  }
+  if (e != hipSuccess) return W4A16_ERR_HIP;
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(256), 0, s, partial, nb, M, argmax);
+  return launched(hipGetLastError());
+}
+
+w4a16_status_t w4a16_dequant(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, const int32_t* rows,
+                             int R, float* out, int N, int K, int group, void* stream) {
+  if (group != 64) return W4A16_ERR_UNSUPPORTED;
+  if (N < 0 || K < 64 || K % 64 != 0) return W4A16_ERR_SHAPE;
+  if (rows && R < 0) return W4A16_ERR_SHAPE;
+  const int nrows = rows ? R : N;
+  if (nrows == 0) return W4A16_OK;
+  if (!qw || !scales || !biases || !out) return W4A16_ERR_NULL;
+  if (!aligned(qw, 4) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(out, 16) ||
+      (rows && !aligned(rows, 4)))
+    return W4A16_ERR_ALIGN;
+  const size_t words = (size_t)nrows * (size_t)(K / 8);
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, qw, scales,
+                     biases, rows, nrows, out, N, K);
+  return launched(hipGetLastError());
+}
+
+w4a16_status_t w4a16_pack(const uint8_t* codes, uint32_t* qw, int N, int K, void* stream) {
+  if (N < 0 || K < 0 || K % 8 != 0) return W4A16_ERR_SHAPE;
+  if (N == 0 || K == 0) return W4A16_OK;
+  if (!codes || !qw) return W4A16_ERR_NULL;
+  if (!aligned(qw, 4)) return W4A16_ERR_ALIGN;
+  const size_t words = (size_t)N * (size_t)(K / 8);
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, codes, qw, words);
+  return launched(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 group-affine decode library.
+ *
+ * The operation (letters: M activation rows, N output features, K reduction):
+ *
+ *     y[m, n] = sum_k x[m, k] * w[n, k],    w[n, k] = q[n, k] * s[n, g] + b[n, g],
+ *     g = floor(k / 64)
+ *
+ * as defined on "Week 2 Day 2: Keep W4 Packed" (tiny-llm book), sections
+ * "Group-Wise Affine Quantization", "Reconstruct a Stored Group" (w = q s + b,
+ * unsigned 4-bit code, signed scale used as stored) and "Quantized Matrix
+ * Multiplication" (C = A B^T with the dequantized B), at the group size 64 of
+ * the Gemma-4 megakernel page ("Usage").  M is 1 for greedy decode or k+1 for
+ * a speculative-verify batch (Gemma-4 megakernel page, "What it does": the
+ * weights stream once for all M rows).
+ *
+ * Data layout (all row-major, contiguous, caller-owned DEVICE memory):
+ *   x       bf16 bits (uint16_t)  [M][K]
+ *   qw      uint32                [N][K/8]   word j of row n holds codes
+ *                                            k = 8j .. 8j+7, code 8j+i in bits
+ *                                            4i .. 4i+3 ("Packed Storage Layout")
+ *   scales  bf16 bits             [N][K/64]
+ *   biases  bf16 bits             [N][K/64]
+ *   y       bf16 bits or fp32     [M][N]
+ *
+ * Arithmetic contract: each weight is dequantized as one fp32 fused
+ * multiply-add fma(s, q, b) (bit-exact with w4a16_dequant), products are
+ * accumulated in fp32 in an order fixed by (N, K) alone, and the bf16 output
+ * is the round-to-nearest-even of the fp32 result.  Hence row m of an M-row
+ * call is bitwise equal to a 1-row call on x[m] (batch invariance, which the
+ * lossless speculative decoding of the Gemma-4 megakernel page relies on).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a device pointer owned by the caller; the library
+ *     allocates nothing, keeps no state between calls and never synchronizes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); work
+ *     is enqueued on it and the call returns immediately.
+ *   - Argument errors are detected before anything is enqueued; on any error
+ *     nothing is launched and nothing is written.
+ *   - Calls are re-entrant.  Outputs must not alias inputs.
+ *   - Empty problems (M == 0 or N == 0) succeed without launching.
+ *   - Alignment: qw 16 bytes; x 4 bytes; scales, biases 2 bytes; y 2 bytes
+ *     (bf16) or 4 bytes (fp32); ids, argmax 4 bytes; workspace 8 bytes.
+ *   - Only group == 64 and 4-bit codes are supported.
+ *   - Asynchronous device faults surface at the caller's next synchronization.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+#define W4A16_MAX_M 8
+
+typedef enum w4a16_status {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = 1,        /* a required pointer is NULL */
+    W4A16_ERR_SHAPE = 2,       /* a size is negative, K is not a positive multiple of 64,
+                                  top_k/E/R out of range, or a size overflows */
+    W4A16_ERR_UNSUPPORTED = 3, /* group != 64, M > 8, or an unknown out_dtype */
+    W4A16_ERR_ALIGN = 4,       /* a pointer violates the alignment above */
+    W4A16_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    W4A16_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} w4a16_status_t;
+
+typedef enum w4a16_out {
+    W4A16_OUT_BF16 = 0,        /* y holds bf16 bits, round-to-nearest-even of the fp32 sum */
+    W4A16_OUT_F32 = 1          /* y holds the fp32 sum itself (same arithmetic) */
+} w4a16_out_t;
+
+/*
+ * Dense product, 1 <= M <= 8 (qmv at M = 1, skinny qmm at M = 2..8).
+ * Definition: "Quantized Matrix Multiplication" / "Computation Flow" on the
+ * tiny-llm W4 page, with the group size of the Gemma-4 page.
+ * y: [M][N], bf16 or fp32 per out_dtype.
+ */
+w4a16_status_t w4a16_matmul(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
+                            const uint16_t *biases, void *y, int out_dtype, int M, int N, int K,
+                            int group, void *stream);
+
+/*
+ * Routed (expert-gathered) product for MoE decode: the routed-expert matvec
+ * (mul_mv_id) of the hy4-preview-metal page's kernel table.
+ *   qw [E][N][K/8], scales/biases [E][N][K/64]  (expert e = slab e)
+ *   ids int32 [M][top_k], each in [0, E)
+ *   x   [M][K] shared by a token's slots (x_per_slot == 0), or
+ *       [M][top_k][K] one row per slot (x_per_slot != 0)
+ *   y   [M][top_k][N]:  y[m][j][:] = W_{ids[m][j]} . x[m] (or x[m][j])
+ * Each distinct expert's weights are streamed once for all slots routed to
+ * it.  No routing weights are applied.  An id outside [0, E) is a
+ * precondition violation: the slot's output row is filled with NaN.
+ * 1 <= M <= 8, 1 <= top_k <= 64, 1 <= E.
+ */
+w4a16_status_t w4a16_matmul_id(const uint16_t *x, int x_per_slot, const uint32_t *qw,
+                               const uint16_t *scales, const uint16_t *biases, const int32_t *ids,
+                               void *y, int out_dtype, int M, int top_k, int E, int N, int K,
+                               int group, void *stream);
+
+/*
+ * Bytes of device workspace w4a16_lmhead_argmax needs for this shape
+ * (0 when the arguments are invalid).
+ */
+size_t w4a16_lmhead_argmax_workspace_bytes(int M, int N, int K, int group);
+
+/*
+ * Tied LM head with fused per-row argmax: the 4-bit vocabulary projection
+ * with in-kernel argmax of the Gemma-4 megakernel page ("What it does", draft
+ * kernel), the tied output head of the tiny-llm page (Task 1, as_linear).
+ *   logits [M][N] (bf16 or fp32 per out_dtype), or NULL to skip writing them
+ *   argmax int32 [M]: index of the largest fp32 logit of row m; ties go to the
+ *          lowest index; a NaN logit ranks above every number.
+ *   workspace: at least w4a16_lmhead_argmax_workspace_bytes(M, N, K, group)
+ *          bytes of device memory; its contents need no initialization and
+ *          are scratch for this call only.
+ * Two kernels run on `stream`: the product with per-block partial argmax,
+ * then an ordered finalize.  Deterministic.
+ */
+w4a16_status_t w4a16_lmhead_argmax(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
+                                   const uint16_t *biases, void *logits, int out_dtype,
+                                   int32_t *argmax, void *workspace, size_t workspace_bytes,
+                                   int M, int N, int K, int group, void *stream);
+
+/*
+ * Dequantized weights out[r][k] = fma(s, q, b) in fp32 for rows[r] (rows ==
+ * NULL: every row, R = N), the same value the products use for each weight
+ * ("Reconstruct a Stored Group").  Also the quantized row gather of an
+ * embedding lookup (tiny-llm page, Task 1: dequantize selected rows without
+ * expanding the table).  A row index outside [0, N) writes NaN to that row.
+ * out: fp32 [R][K], 16-byte aligned; qw needs only 4-byte alignment here.
+ */
+w4a16_status_t w4a16_dequant(const uint32_t *qw, const uint16_t *scales, const uint16_t *biases,
+                             const int32_t *rows, int R, float *out, int N, int K, int group,
+                             void *stream);
+
+/*
+ * Packed-weight loader: codes uint8 [N][K] (low 4 bits used) -> qw uint32
+ * [N][K/8] in the layout above ("Packed Storage Layout").  K % 8 == 0.
+ */
+w4a16_status_t w4a16_pack(const uint8_t *codes, uint32_t *qw, int N, int K, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *w4a16_status_str(w4a16_status_t s);
+
+/* W4A16_ABI_VERSION of the loaded library. */
+int w4a16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,390 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every input is seeded and synthetic (module ``synthetic``); no expected value
+comes from the GPU.  Each test prints the case it is about to run.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import decode_w4a16_affine_amd as w4
+import synthetic
+from parity import (DevWeights, check_argmax, check_bf16, check_f32, dev_bf16, dev_i32, dev_qw, host_bits,
+                    host_f32, oracle_qmm, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w4.lib()
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_mm(dw, x_bits, N, f32=False):
+    x = dev_bf16(x_bits)
+    y = torch.empty((x.shape[0], N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    w4.w4a16_matmul(x, dw.qw, dw.s, dw.b, y)
+    torch.cuda.synchronize()
+    return host_f32(y) if f32 else host_bits(y)
+
+
+def full_check(orc, w, x_bits, y64, absy, what):
+    dw = DevWeights(w)
+    y32 = run_mm(dw, x_bits, w.qw.shape[0], f32=True)
+    yb = run_mm(dw, x_bits, w.qw.shape[0], f32=False)
+    rel = check_f32(y32, y64, absy, what)
+    ex = check_bf16(orc, yb, y64, absy, w.K, what)
+    say(f"  {what}: max |err|/sum|wx| = {rel:.2e}, bf16 exempt {ex}/{yb.size}")
+    # bf16 output is the RNE of the fp32 output, bit for bit
+    assert np.array_equal(yb, synthetic.bf16_bits(y32)), what
+    return dw, y32, yb
+
+
+# ---------------------------------------------------------------------------
+# Layout and dequantization
+# ---------------------------------------------------------------------------
+
+def test_pack_matches_oracle(orc):
+    for (N, K) in [(37, 264), (5, 8), (256, 512)]:
+        say(f"pack N={N} K={K}")
+        codes = synthetic.random_codes(N, K, seed=N)
+        qw = w4.pack(torch.from_numpy(codes).cuda())
+        torch.cuda.synchronize()
+        got = qw.cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, orc.pack_rows(codes))
+
+
+def crafted_scales(N, G, seed):
+    """bf16 scale/bias patterns over a wide range: signs, zero, subnormal, |s| >= 2^100."""
+    g = np.random.default_rng(seed)
+    e_s = g.integers(90, 160, size=(N, G))
+    e_b = g.integers(90, 160, size=(N, G))
+    s = ((g.integers(0, 2, size=(N, G)) << 15) | (e_s << 7) | g.integers(0, 128, size=(N, G))).astype(np.uint16)
+    b = ((g.integers(0, 2, size=(N, G)) << 15) | (e_b << 7) | g.integers(0, 128, size=(N, G))).astype(np.uint16)
+    s[0, 0] = 0x0000
+    s[0, 1 % G] = 0x8000
+    s[1 % N, 0] = 0x0003                      # subnormal scale
+    s[2 % N, 0] = 0x7180                      # 2^100: takes the plain path
+    s[3 % N, 0] = 0xF1C0                      # -1.5 * 2^100
+    b[3 % N, 0] = 0x0001
+    return s, b
+
+
+def test_dequant_bit_exact(orc):
+    for (N, K, kind) in [(256, 512, "config"), (64, 2560, "crafted"), (9, 192, "crafted")]:
+        say(f"dequant N={N} K={K} {kind}")
+        w = synthetic.quantized_weights(N, K, seed=N + K)
+        if kind == "crafted":
+            w.scales, w.biases = crafted_scales(N, K // 64, seed=N)
+        got = w4.dequant(dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases))
+        torch.cuda.synchronize()
+        ref = orc.dequant_rows(w.qw, w.scales, w.biases, K)
+        assert np.array_equal(host_f32(got).view(np.uint32), ref.view(np.uint32))
+    say("dequant row gather with an out-of-range row")
+    w = synthetic.quantized_weights(40, 320, seed=5)
+    rows = np.array([39, 0, 17, 40, -1, 17], dtype=np.int32)
+    got = host_f32(w4.dequant(dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases), rows=dev_i32(rows)))
+    ref = orc.dequant_rows(w.qw, w.scales, w.biases, 320, rows=[39, 0, 17, 17])
+    assert np.array_equal(got[[0, 1, 2, 5]].view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(got[3]).all() and np.isnan(got[4]).all()
+
+
+# ---------------------------------------------------------------------------
+# Dense product: the five workloads and their edges
+# ---------------------------------------------------------------------------
+
+def test_tiny_config(orc):
+    say("tiny qmv M=1 N=256 K=512 seed 0")
+    w = synthetic.quantized_weights(256, 512, seed=0)
+    x = synthetic.activations(1, 512, seed=0)
+    y64, absy = orc.qmm(x, w.qw, w.scales, w.biases)
+    full_check(orc, w, x, y64, absy, "tiny")
+
+
+@pytest.mark.parametrize("name", ["q", "k", "gate_up", "down"])
+def test_decode_projections_and_verify_batches(orc, name):
+    N, K = synthetic.PROJECTIONS[name]
+    tag = (list(synthetic.PROJECTIONS).index(name),)
+    w = synthetic.quantized_weights(N, K, seed=0, tag=tag)
+    x5 = synthetic.activations(5, K, seed=0, tag=tag)
+    say(f"decode projection {name} N={N} K={K}: oracle")
+    y64, absy = oracle_qmm(orc, x5, w)
+    dw = None
+    singles32, singlesb = [], []
+    for m in range(5):
+        say(f"  {name} M=1 row {m}")
+        dw, y32, yb = full_check(orc, w, x5[m:m + 1], y64[m:m + 1], absy[m:m + 1], f"{name} M=1 row{m}")
+        singles32.append(y32[0]); singlesb.append(yb[0])
+    for M in synthetic.VERIFY_M:
+        say(f"  {name} verify M={M}")
+        _, y32, yb = full_check(orc, w, x5[:M], y64[:M], absy[:M], f"{name} M={M}")
+        for m in range(M):   # batch invariance: bitwise equal to the 1-row call
+            assert np.array_equal(y32[m].view(np.uint32), singles32[m].view(np.uint32)), (name, M, m)
+            assert np.array_equal(yb[m], singlesb[m]), (name, M, m)
+
+
+RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560)]
+
+
+@pytest.mark.parametrize("N,K", RAGGED)
+def test_every_M_ragged_shapes_batch_invariant(orc, N, K):
+    w = synthetic.quantized_weights(N, K, seed=N * 7 + K)
+    x = synthetic.activations(8, K, seed=N + K)
+    say(f"ragged N={N} K={K}: oracle")
+    y64, absy = oracle_qmm(orc, x, w)
+    dw = DevWeights(w)
+    ref32 = None
+    for M in range(1, 9):
+        say(f"  ragged N={N} K={K} M={M}")
+        y32 = run_mm(dw, x[:M], N, f32=True)
+        check_f32(y32, y64[:M], absy[:M], f"N={N} K={K} M={M}")
+        yb = run_mm(dw, x[:M], N, f32=False)
+        check_bf16(orc, yb, y64[:M], absy[:M], K, f"N={N} K={K} M={M}")
+        if M == 1:
+            ref32 = [run_mm(dw, x[m:m + 1], N, f32=True)[0] for m in range(8)]
+        for m in range(M):
+            assert np.array_equal(y32[m].view(np.uint32), ref32[m].view(np.uint32)), (N, K, M, m)
+
+
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_long_reduction_segments(orc, M):
+    # K beyond one LDS segment for every M, with a ragged final segment
+    N, K = 300, 16384 + 3 * 64
+    w = synthetic.quantized_weights(N, K, seed=77)
+    x = synthetic.activations(8, K, seed=78)
+    rows = np.arange(0, N, 3, dtype=np.int32)
+    say(f"long K={K} M={M}: oracle on {len(rows)} rows")
+    y64, absy = oracle_qmm(orc, x[:M], w, rows=rows)
+    dw = DevWeights(w)
+    y32 = run_mm(dw, x[:M], N, f32=True)
+    check_f32(y32[:, rows], y64, absy, f"long K M={M}")
+    yb = run_mm(dw, x[:M], N)
+    check_bf16(orc, yb[:, rows], y64, absy, K, f"long K M={M}")
+    for m in range(M):
+        y1 = run_mm(dw, x[m:m + 1], N, f32=True)
+        assert np.array_equal(y1[0].view(np.uint32), y32[m].view(np.uint32)), m
+
+
+@pytest.mark.parametrize("M", synthetic.SQUARE["M"])
+def test_square_16384(orc, M):
+    N = K = 16384
+    w = synthetic.quantized_weights(N, K, seed=0, tag=(16384,))
+    x = synthetic.activations(8, K, seed=0, tag=(16384,))
+    rows = np.random.default_rng(1).choice(N, size=384, replace=False).astype(np.int32)
+    rows.sort()
+    say(f"square 16384^2 M={M}: oracle on {len(rows)} rows")
+    y64, absy = oracle_qmm(orc, x[:M], w, rows=rows)
+    dw = DevWeights(w)
+    y32 = run_mm(dw, x[:M], N, f32=True)
+    check_f32(y32[:, rows], y64, absy, f"square M={M}")
+    yb = run_mm(dw, x[:M], N)
+    check_bf16(orc, yb[:, rows], y64, absy, K, f"square M={M}")
+    assert np.array_equal(yb, synthetic.bf16_bits(y32))
+    if M > 1:
+        for m in range(M):
+            y1 = run_mm(dw, x[m:m + 1], N, f32=True)
+            assert np.array_equal(y1[0].view(np.uint32), y32[m].view(np.uint32)), m
+
+
+def test_closed_forms_on_gpu(orc):
+    say("closed forms: identity-like weights copy x")
+    N, K, M = 64, 128, 3
+    codes = np.zeros((N, K), dtype=np.uint8)
+    codes[np.arange(N), np.arange(N)] = 1
+    qw = orc.pack_rows(codes)
+    ones = synthetic.bf16_bits(np.ones((N, K // 64), dtype=np.float32))
+    zeros = np.zeros((N, K // 64), dtype=np.uint16)
+    x = synthetic.activations(M, K, seed=31)
+    y = w4.matmul(dev_bf16(x), dev_qw(qw), dev_bf16(ones), dev_bf16(zeros))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y), x[:, :N])
+
+    say("closed forms: zero activations give +0")
+    w = synthetic.quantized_weights(300, 640, seed=32)
+    yz = run_mm(DevWeights(w), np.zeros((4, 640), dtype=np.uint16), 300, f32=True)
+    assert np.all(yz == 0) and not np.signbit(yz).any()
+
+    say("closed forms: rows whose dequantized weights are all zero give exactly 0")
+    w = synthetic.quantized_weights(5000, 512, seed=33, bias="exact")
+    w.qw[::7] = 0x88888888                     # q = 8 with b = -8 s: w = 0 exactly
+    x = synthetic.activations(2, 512, seed=33)
+    y32 = run_mm(DevWeights(w), x, 5000, f32=True)
+    assert np.all(y32[:, ::7] == 0)
+    y64, absy = orc.qmm(x, w.qw, w.scales, w.biases, rows=np.arange(0, 5000, 7))
+    assert np.all(y64 == 0) and np.all(absy == 0)
+
+    say("closed forms: all codes equal")
+    for c in (0, 9, 15):
+        w = synthetic.quantized_weights(100, 1024, seed=34 + c)
+        w.qw[:] = np.uint32(int(f"{c:x}" * 8, 16))
+        x = synthetic.activations(2, 1024, seed=34)
+        y64, absy = orc.qmm(x, w.qw, w.scales, w.biases)
+        full_check(orc, w, x, y64, absy, f"codes={c}")
+
+
+def test_deterministic_and_no_stray_writes(orc):
+    N, K, M = 5000, 2560, 3
+    say(f"determinism and guard bands N={N} K={K} M={M}")
+    w = synthetic.quantized_weights(N, K, seed=41)
+    dw = DevWeights(w)
+    x = dev_bf16(synthetic.activations(M, K, seed=41))
+    pad = 4096
+    for dt, sentinel in ((torch.float32, 1234.5), (torch.bfloat16, -7.0)):
+        buf = torch.full((M * N + 2 * pad,), sentinel, dtype=dt, device="cuda")
+        y = buf[pad:pad + M * N].view(M, N)
+        w4.w4a16_matmul(x, dw.qw, dw.s, dw.b, y)
+        first = y.clone()
+        w4.w4a16_matmul(x, dw.qw, dw.s, dw.b, y)
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           y.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+        assert bool((buf[:pad] == sentinel).all()) and bool((buf[pad + M * N:] == sentinel).all())
+
+
+def test_empty_problems_write_nothing():
+    say("empty problems")
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    qw = torch.zeros((16, 16), dtype=torch.int32, device="cuda")
+    s = torch.zeros((16, 2), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((0, 16), 3.0, dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_matmul(x, qw, s, s, y)
+    x1 = torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda")
+    y1 = torch.full((1, 0), 3.0, dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_matmul(x1, qw[:0], s[:0], s[:0], y1)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# LM head with fused argmax
+# ---------------------------------------------------------------------------
+
+def test_lmhead_argmax_config(orc):
+    N, K = synthetic.LM_HEAD["N"], synthetic.LM_HEAD["K"]
+    w = synthetic.quantized_weights(N, K, seed=0, tag=(262144,), bias="exact")
+    x3 = synthetic.activations(3, K, seed=0, tag=(262144,))
+    say(f"lm head N={N} K={K}: oracle (all rows, M=3)")
+    y64, absy = oracle_qmm(orc, x3, w, workers=16)
+    dw = DevWeights(w)
+    for M in synthetic.LM_HEAD["M"]:
+        say(f"  lm head M={M}")
+        xd = dev_bf16(x3[:M])
+        am, logits = w4.lmhead_argmax(xd, dw.qw, dw.s, dw.b, out_dtype=torch.float32)
+        am2, none = w4.lmhead_argmax(xd, dw.qw, dw.s, dw.b, want_logits=False)
+        amb, lb = w4.lmhead_argmax(xd, dw.qw, dw.s, dw.b, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        am = am.cpu().numpy()
+        assert none is None and np.array_equal(am, am2.cpu().numpy()) and np.array_equal(am, amb.cpu().numpy())
+        y32 = host_f32(logits)
+        check_f32(y32, y64[:M], absy[:M], f"lm head logits M={M}")
+        check_bf16(orc, host_bits(lb), y64[:M], absy[:M], K, f"lm head bf16 M={M}")
+        # the argmax is that of the fp32 logits, lowest index on ties
+        for m in range(M):
+            assert am[m] == int(np.flatnonzero(y32[m] == y32[m].max())[0])
+        n = check_argmax(orc, am, y64[:M], absy[:M], f"lm head M={M}")
+        say(f"  lm head M={M}: argmax {am.tolist()}, checked {n}/{M} rows")
+        # logits equal the dense product bit for bit
+        ym = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        w4.w4a16_matmul(xd, dw.qw, dw.s, dw.b, ym)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_f32(ym).view(np.uint32), y32.view(np.uint32))
+
+
+@pytest.mark.parametrize("N", [1, 100, 5000, 70000])
+def test_lmhead_ties_and_planted_maximum(orc, N):
+    K = 512
+    say(f"lm head ties N={N}")
+    w = synthetic.quantized_weights(N, K, seed=N, bias="exact")
+    x = synthetic.activations(2, K, seed=N)
+    xv = synthetic.bf16_values(x)
+    codes = orc.unpack_rows(w.qw, K)
+    star = N // 3
+    codes[star] = np.where(xv[0] > 0, 15, 0)
+    qw = orc.pack_rows(codes)
+    dup = [n for n in (N - 1, star + 1) if n != star and n < N]
+    for d in dup:                                   # later duplicates must lose the tie
+        qw[d] = qw[star]; w.scales[d] = w.scales[star]; w.biases[d] = w.biases[star]
+    am, logits = w4.lmhead_argmax(dev_bf16(x), dev_qw(qw), dev_bf16(w.scales), dev_bf16(w.biases),
+                                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(am[0]) == star
+    y = host_f32(logits)
+    assert int(am[1]) == int(np.flatnonzero(y[1] == y[1].max())[0])
+
+
+# ---------------------------------------------------------------------------
+# Routed (expert-gathered) product
+# ---------------------------------------------------------------------------
+
+def routed_inputs(E, N, K, M, top_k, seed):
+    w = synthetic.quantized_weights(N, K, seed=seed, lead=(E,))
+    x = synthetic.activations(M, K, seed=seed)
+    ids = synthetic.expert_ids(M, top_k, E, seed=seed)
+    return w, x, ids
+
+
+def run_id(dw_stack, x_bits, ids, N, f32=True, x_per_slot=False):
+    y = w4.matmul_id(dev_bf16(x_bits), dw_stack[0], dw_stack[1], dw_stack[2], dev_i32(ids), x_per_slot=x_per_slot,
+                     out_dtype=torch.float32 if f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    return host_f32(y) if f32 else host_bits(y)
+
+
+def test_routed_moe_config(orc):
+    E, N, K, top_k = synthetic.MOE["E"], synthetic.MOE["N"], synthetic.MOE["K"], synthetic.MOE["top_k"]
+    w, x, ids = routed_inputs(E, N, K, 8, top_k, seed=0)
+    say(f"moe E={E} N={N} K={K} top_k={top_k}: oracle M=8")
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(lambda m: orc.qmm_id(x[m:m + 1], w.qw, w.scales, w.biases, ids[m:m + 1]), range(8)))
+    y64 = np.concatenate([r[0] for r in res])
+    absy = np.concatenate([r[1] for r in res])
+    stack = (dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases))
+    say(f"  moe M=8 ids unique experts {len(np.unique(ids))}")
+    y8 = run_id(stack, x, ids, N)
+    check_f32(y8, y64, absy, "moe M=8")
+    yb8 = run_id(stack, x, ids, N, f32=False)
+    check_bf16(orc, yb8, y64, absy, K, "moe M=8")
+    for m in range(8):
+        say(f"  moe M=1 token {m}")
+        y1 = run_id(stack, x[m:m + 1], ids[m:m + 1], N)
+        assert np.array_equal(y1[0].view(np.uint32), y8[m].view(np.uint32)), m      # batch invariance
+    # every slot equals the dense product on its expert, bit for bit
+    for m, j in [(0, 0), (3, 5), (7, 7)]:
+        e = int(ids[m, j])
+        yd = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        w4.w4a16_matmul(dev_bf16(x[m:m + 1]), stack[0][e], stack[1][e], stack[2][e], yd)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_f32(yd)[0].view(np.uint32), y8[m, j].view(np.uint32))
+
+
+def test_routed_variants(orc):
+    E, N, K, M, top_k = 6, 700, 576, 5, 3
+    w, x, _ = routed_inputs(E, N, K, M, top_k, seed=9)
+    stack = (dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases))
+    ids = np.array([[0, 1, 2], [2, 2, 5], [5, 0, 1], [3, 3, 3], [1, 4, 0]], dtype=np.int32)  # shared + duplicate ids
+    say("routed: shared and duplicate ids")
+    y64, absy = orc.qmm_id(x, w.qw, w.scales, w.biases, ids)
+    y = run_id(stack, x, ids, N)
+    check_f32(y, y64, absy, "routed dup")
+    say("routed: one input row per slot")
+    xs = synthetic.activations(M * top_k, K, seed=10).reshape(M, top_k, K)
+    y64s, abss = orc.qmm_id(xs, w.qw, w.scales, w.biases, ids, x_per_slot=True)
+    ys = run_id(stack, xs, ids, N, x_per_slot=True)
+    check_f32(ys, y64s, abss, "routed per-slot")
+    check_bf16(orc, run_id(stack, xs, ids, N, f32=False, x_per_slot=True), y64s, abss, K, "routed per-slot bf16")
+    say("routed: out-of-range id fills its slot with NaN")
+    bad = ids.copy()
+    bad[1, 1] = E
+    bad[4, 0] = -3
+    yb = run_id(stack, x, bad, N)
+    assert np.isnan(yb[1, 1]).all() and np.isnan(yb[4, 0]).all()
+    keep = np.ones((M, top_k), dtype=bool)
+    keep[1, 1] = keep[4, 0] = False
+    assert np.array_equal(yb[keep].view(np.uint32), y[keep].view(np.uint32))

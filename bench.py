@@ -114,29 +114,18 @@ def time_graph(torch, g, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def kernel_durations(torch, w4, stack, layers: int, reps: int = 20):
-    """Average duration of each projection's launch, measured with events
-    recorded on the launch stream immediately around single eager launches
-    (layers rotate so every launch is cold)."""
+def kernel_durations(torch, w4, stack, layers: int, reps: int = 10):
+    """Average duration of one launch of each projection: a graph holding that
+    projection's launch for every layer (cold weights) is replayed `reps`
+    times between two events on the replay stream, and the elapsed time is
+    divided by the number of launches.  Graph replays leave no measurable
+    gap between consecutive kernels, so this is the kernel duration."""
     out = {}
-    s = torch.cuda.current_stream()
     for p in synthetic.LAYER_ORDER:
-        d = stack[p]
-        x, y = d["x"][:1], d["y"][:1]
-        times = []
-        for r in range(reps + 3):
-            l = r % layers
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(s)
-            w4.w4a16_matmul(x, d["qw"][l], d["s"][l], d["b"][l], y, stream=s)
-            e1.record(s)
-            e1.synchronize()
-            if r >= 3:
-                times.append(e0.elapsed_time(e1) * 1e3)
-        out[p] = float(np.median(times))
+        g = capture(torch, make_step(w4, stack, 1, layers, only=(p,)))
+        out[p] = time_graph(torch, g, reps, 2) * 1e3 / layers
+        del g
     return out
-
 
 def cpu_baseline(host0, seconds: float = 10.0):
     """The oracle, as it stands, on one host core over layer 0's projections."""
@@ -172,10 +161,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device-to-device copy (a known-size reference for "
+                         "memory-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the product shards by rows or experts; see the design notes)", file=sys.stderr)
+              "(a multi-GPU deployment would shard output rows or experts; this benchmark runs on one)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -202,17 +194,18 @@ def main():
         log(f"M={M}: {ms:.4f} ms/step, {results[M]['gbs']:.1f} GB/s")
         del g
 
-    # Dominant kernel: per-launch durations, events around single launches.
+    # Dominant kernel (largest share of the M=1 step): one kernel symbol per
+    # schedule, so projections are grouped by the kernel that serves them.
     dur = kernel_durations(torch, w4, stack, L)
-    # gate_up runs the wide-matrix kernel; q, k, v, o, down share the K-split one.
-    wide = ["gate_up"]
-    narrow = [p for p in synthetic.LAYER_ORDER if p not in wide]
-    groups = {"wide (gate_up)": wide, "K-split (q,k,v,o,down)": narrow}
+    groups = {}
+    for p in synthetic.LAYER_ORDER:
+        N, K = synthetic.PROJECTIONS[p]
+        groups.setdefault(w4.w4a16_schedule_name(1, N, K), []).append(p)
     per_group = {}
     for name, ps in groups.items():
-        t = sum(dur[p] for p in ps)
-        b = sum(call_bytes(1, *synthetic.PROJECTIONS[p]) for p in ps)
-        per_group[name] = dict(us_total=t, bytes_total=b, launches=len(ps))
+        per_group[name] = dict(us_total=sum(dur[p] for p in ps),
+                               bytes_total=sum(call_bytes(1, *synthetic.PROJECTIONS[p]) for p in ps),
+                               launches=len(ps), projections=ps)
     dom = max(per_group, key=lambda k: per_group[k]["us_total"])
     pg = per_group[dom]
     avg_us = pg["us_total"] / pg["launches"]
@@ -220,10 +213,22 @@ def main():
     achieved = avg_bytes / (avg_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_GBS, 4), traffic=None,
-                    kernel=dom, avg_launch_us=round(avg_us, 3), avg_launch_bytes=int(avg_bytes),
+                    kernel=dom, serves=pg["projections"], avg_launch_us=round(avg_us, 3),
+                    avg_launch_bytes=int(avg_bytes),
                     per_projection_us={p: round(v, 3) for p, v in dur.items()},
                     per_projection_gbs={p: round(call_bytes(1, *synthetic.PROJECTIONS[p]) / (v * 1e-6) / 1e9, 1)
-                                        for p, v in dur.items()})
+                                        for p, v in dur.items()},
+                    per_projection_frac={p: round(call_bytes(1, *synthetic.PROJECTIONS[p]) / (v * 1e-6) / 1e9
+                                                  / PEAK_GBS, 4) for p, v in dur.items()})
+
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     cpu = None
     if not args.no_cpu_baseline:

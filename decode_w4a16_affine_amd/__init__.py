@@ -31,7 +31,7 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_
 
 EXPORTS = ("w4a16_matmul", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
            "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_pack", "w4a16_status_str",
-           "w4a16_abi_version")
+           "w4a16_abi_version", "w4a16_schedule_name")
 
 
 class W4A16Error(RuntimeError):
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.w4a16_status_str.argtypes = [_int]
         L.w4a16_abi_version.restype = _int
         L.w4a16_abi_version.argtypes = []
+        L.w4a16_schedule_name.restype = ctypes.c_char_p
+        L.w4a16_schedule_name.argtypes = [_int, _int, _int, _int]
         _lib = L
     return _lib
 
@@ -178,6 +180,10 @@ def w4a16_status_str(status: int) -> str:
 
 def w4a16_abi_version() -> int:
     return int(lib().w4a16_abi_version())
+
+
+def w4a16_schedule_name(M: int, N: int, K: int, group: int = GROUP) -> str:
+    return lib().w4a16_schedule_name(M, N, K, group).decode()
 
 
 # ---- allocating conveniences (torch allocates; the library computes) ------------

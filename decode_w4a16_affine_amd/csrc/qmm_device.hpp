@@ -34,7 +34,6 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kRowLanes = 16;
 constexpr int kSlots = kWave / kRowLanes;      // row groups per wave
 constexpr int kMaxM = 8;
-constexpr int kLdsXFloats = 15360;             // activation staging budget: 60 KiB per block
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -107,33 +106,15 @@ struct XRows {
   const uint16_t* p[M];
 };
 
-// Stage x[m][k0 .. k0+klen) into LDS as fp32.  Layout (float4 units):
-// xs[(m * 8 + piece) * cseg + c] holds k = k0 + 32c + 4*piece .. +3, so lanes
-// reading consecutive chunks of one piece touch consecutive 16-byte words.
-template <int M>
-__device__ __forceinline__ void stage_x(float4* xs, const XRows<M>& xr, int k0, int klen) {
-  const int cseg = klen >> 5;
-  const int pairs = klen >> 1;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(xr.p[m] + k0);
-    for (int j = threadIdx.x; j < pairs; j += kThreads) {
-      const uint32_t v = src[j];
-      const int kk = 2 * j;
-      const int c = kk >> 5, piece = (kk >> 2) & 7, e = kk & 3;
-      float2* dst = reinterpret_cast<float2*>(reinterpret_cast<float*>(xs + (m * 8 + piece) * cseg + c) + e);
-      *dst = make_float2(bf16_lo(v), bf16_hi(v));
-    }
-  }
+// Buffer resource for a raw byte range (gfx9 family descriptor word 3).
+// Loads whose offset + size exceed `bytes` return zero and touch no memory.
+// The size goes through readfirstlane so the whole descriptor stays in SGPRs
+// (a descriptor the compiler cannot prove uniform costs a waterfall loop per load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
-
-// Weights of U chunks x R rows for one lane, in registers.
-template <int U, int R>
-struct Batch {
-  uint4 w[U][R];
-  uint32_t s[U][R];
-  uint32_t b[U][R];
-};
+constexpr uint32_t kOffNone = 0x80000000u;    // an offset beyond every range: the load returns 0
 
 struct RowSrc {
   const uint32_t* __restrict__ qw;
@@ -143,30 +124,14 @@ struct RowSrc {
   int K;
 };
 
-template <int U, int R, int LPR>
-__device__ __forceinline__ void load_batch(Batch<U, R>& bt, const RowSrc& src, int row_first, int cb, int cseg,
-                                           int cbase, int L) {
-  const size_t wpr = (size_t)(src.K >> 3);
-  const int gpr = src.K >> 6;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = cb + u * LPR + L;
-    const int cg = cbase + c;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int n = row_first + r;
-      if (c < cseg && n < src.N) {
-        bt.w[u][r] = *reinterpret_cast<const uint4*>(src.qw + (size_t)n * wpr + (size_t)cg * 4);
-        bt.s[u][r] = src.scales[(size_t)n * gpr + (cg >> 1)];
-        bt.b[u][r] = src.biases[(size_t)n * gpr + (cg >> 1)];
-      } else {
-        bt.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
-        bt.s[u][r] = 0u;
-        bt.b[u][r] = 0u;
-      }
-    }
-  }
-}
+// One K-tile of one lane: CPL chunks (16-byte code loads) for each of R rows,
+// plus each chunk's group scale and bias as bf16 bits.
+template <int CPL, int R>
+struct Tile {
+  uint4 w[CPL][R];
+  uint32_t s[CPL][R];
+  uint32_t b[CPL][R];
+};
 
 template <int M, int R, bool FAST>
 __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R], const float (&s)[R],
@@ -204,68 +169,117 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
   }
 }
 
-template <int M, int U, int R, int LPR>
-__device__ __forceinline__ void compute_batch(float (&acc)[R][M], const Batch<U, R>& bt, const float4* xs, int cb,
-                                              int cseg, int L) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = cb + u * LPR + L;
-    if (c < cseg) {
-      float s[R], b[R];
-      bool plain = false;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        s[r] = __uint_as_float(bt.s[u][r] << 16);
-        b[r] = __uint_as_float(bt.b[u][r] << 16);
-        plain |= needs_plain(s[r]);
-      }
-      if (__any(plain))
-        chunk_fma<M, R, false>(acc, bt.w[u], s, b, xs + c, cseg);
-      else
-        chunk_fma<M, R, true>(acc, bt.w[u], s, b, xs + c, cseg);
-    }
-  }
-}
-
 // Full-row sums for the R rows of this lane's row group.
+//
+// Lane L of a row (L = t for KSPLIT 1, wave*16 + t for KSPLIT 4) owns the
+// 16-byte chunks c = L, L + LPR, L + 2 LPR, ... of the row and accumulates
+// them in ascending order; the row is walked in K-tiles of CPL * LPR chunks.
+// Per K-tile: the activation loads are issued first, then every weight load
+// of the tile (straight-line, range-checked buffer loads, so the wait for
+// chunk j never waits for chunk j+1), then x is converted into LDS and the
+// chunks are consumed in order as they arrive.
+//
 // KSPLIT == 1: on return every lane of the row group holds the sums.
-// KSPLIT == 4: the four waves of the block share the rows; on return every
-//              lane of every wave holds the sums (combined in wave order).
-// Must be called by all threads of the block (it synchronizes).
-template <int M, int R, int U, int KSPLIT>
-__device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src, int kseg,
-                                           int row_first, float4* xs, float* red) {
+// KSPLIT == 4: the four waves share the rows; on return every lane of every
+//              wave holds the sums (combined in wave order).
+// xs must hold M * 8 * CPL * LPR float4.  Call with all threads (barriers).
+template <int M, int R, int CPL, int KSPLIT>
+__device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
+                                           int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
+  constexpr int KTILE = CPL * LPR * 32;                       // codes per K-tile
+  constexpr int XL = (KTILE / 8 + kThreads - 1) / kThreads;   // 16-byte x loads per thread per row
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = lane & (kRowLanes - 1);
   const int slot = lane / kRowLanes;
   const int L = KSPLIT == 1 ? t : wave * kRowLanes + t;
+  const int K = src.K;
+  const uint32_t wpr = (uint32_t)(K >> 3);     // code words per row
+  const uint32_t gpr = (uint32_t)(K >> 6);     // groups per row
+
+  // Rows of this wave: [wave_row0, wave_row0 + kSlots*R); the resources end
+  // at the last real row, so loads of rows >= N return zero.
+  const int wave_row0 = block_row0 + (KSPLIT == 1 ? wave * kSlots * R : 0);
+  const int nrows = max(0, min(kSlots * R, src.N - wave_row0));
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(src.qw + (size_t)wave_row0 * wpr, (uint32_t)nrows * wpr * 4u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.scales + (size_t)wave_row0 * gpr, (uint32_t)nrows * gpr * 2u);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(src.biases + (size_t)wave_row0 * gpr, (uint32_t)nrows * gpr * 2u);
+
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-  const int K = src.K;
-  for (int k0 = 0; k0 < K; k0 += kseg) {
-    const int klen = min(kseg, K - k0);
+  for (int k0 = 0; k0 < K; k0 += KTILE) {
+    const int klen = min(KTILE, K - k0);
     const int cseg = klen >> 5;
     const int cbase = k0 >> 5;
-    const int step = LPR * U;
-    const int nb = (cseg + step - 1) / step;
-    Batch<U, R> A, B;
-    // The first weights of the segment are requested before the activations
-    // are staged, so the two latencies overlap.
-    load_batch<U, R, LPR>(A, src, row_first, 0, cseg, cbase, L);
+    const int xq = klen >> 3;                  // 16-byte x pieces per row in this tile
+
+    // 1. activations of this tile (clamped indices: no branches around loads)
+    uint4 xv[M][XL];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+        xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + k0)[i];
+      }
+
+    // 2. every weight load of the tile
+    Tile<CPL, R> tl;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = L + j * LPR;
+      const bool ok = c < cseg;
+      const uint32_t cg = (uint32_t)(cbase + c);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t lr = (uint32_t)(slot * R + r);
+        const uint32_t oq = ok ? (lr * wpr + cg * 4u) * 4u : kOffNone;
+        const uint32_t og = ok ? (lr * gpr + (cg >> 1)) * 2u : kOffNone;
+        tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, oq, 0, 0));
+        tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, og, 0, 0);
+        tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(rb, og, 0, 0);
+      }
+    }
+
+    // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * cseg + c]
+    //    holds k = k0 + 32c + 4 piece .. +3, so lanes reading consecutive chunks
+    //    of one piece touch consecutive 16-byte words.
     __syncthreads();  // every wave is done with the previous contents of xs
-    stage_x<M>(xs, xr, k0, klen);
+    // Threads past the end repeat the last piece (same value, same address).
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+        const int kk = 8 * i;
+        const int c = kk >> 5, piece = (kk >> 2) & 7;
+        const uint4 v = xv[m][j];
+        xs[(m * 8 + piece) * cseg + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+        xs[(m * 8 + piece + 1) * cseg + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+      }
     __syncthreads();
-    for (int ib = 0; ib < nb; ib += 2) {
-      if (ib + 1 < nb) load_batch<U, R, LPR>(B, src, row_first, (ib + 1) * step, cseg, cbase, L);
-      compute_batch<M, U, R, LPR>(acc, A, xs, ib * step, cseg, L);
-      if (ib + 1 < nb) {
-        if (ib + 2 < nb) load_batch<U, R, LPR>(A, src, row_first, (ib + 2) * step, cseg, cbase, L);
-        compute_batch<M, U, R, LPR>(acc, B, xs, (ib + 1) * step, cseg, L);
+
+    // 4. consume the chunks in ascending order
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = L + j * LPR;
+      if (c < cseg) {
+        float s[R], b[R];
+        bool plain = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          s[r] = __uint_as_float(tl.s[j][r] << 16);
+          b[r] = __uint_as_float(tl.b[j][r] << 16);
+          plain |= needs_plain(s[r]);
+        }
+        if (__any(plain))
+          chunk_fma<M, R, false>(acc, tl.w[j], s, b, xs + c, cseg);
+        else
+          chunk_fma<M, R, true>(acc, tl.w[j], s, b, xs + c, cseg);
       }
     }
   }

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
 
 #include "qmm_device.hpp"
 #include "w4a16.h"
@@ -13,30 +14,35 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Schedules.  KSPLIT (how many row groups share one row) fixes a row's
-// arithmetic and is a function of (N, K) only; R (rows per lane) and U
-// (chunks per lane per batch) only change how much is in flight and may
-// depend on M.
+// arithmetic and is a function of (N, K) only.  R (rows per lane) and CPL
+// (chunks per lane per K-tile) only change how much is in flight and how
+// activations are staged, and may depend on M.
 // ---------------------------------------------------------------------------
 
 constexpr int kNarrowN = 4096;
 
 int ksplit_for(int N, int /*K*/) { return N <= kNarrowN ? 4 : 1; }
 
-constexpr int cfg_R(int M, int ksplit) { return ksplit == 4 ? 2 : (M <= 2 ? 2 : 4); }
-constexpr int cfg_U(int M, int ksplit) { return ksplit == 4 ? 1 : (M <= 2 ? 2 : 1); }
+// Schedules measured on MI355X (cold weights, back-to-back launches).  Class 0:
+// the default; class 1: very tall matrices (N >= 131072, vocabulary heads),
+// where two rows per lane win for KSPLIT 1, and long rows (K > 4096) for
+// KSPLIT 4, where a whole row fits one K-tile.
+template <int M, int KSPLIT, int CLS>
+struct Sched {
+  static constexpr int R = KSPLIT == 1 ? (CLS == 1 && M <= 5 ? 2 : 1) : 1;
+  static constexpr int CPL = KSPLIT == 1 ? (M == 1 ? (CLS == 1 ? 5 : 8) : M <= 3 ? 5 : 3)
+                                         : (M <= 3 ? (CLS == 1 && M == 1 ? 5 : 2) : 1);
+};
 
-// Activation segment length: a multiple of the chunk-interleave period
-// (32 codes x 16 x KSPLIT) so segmenting never changes a lane's chunk order.
-int kseg_for(int M, int K, int ksplit) {
-  const int unit = 32 * kRowLanes * ksplit;
-  int cap = (kLdsXFloats / M) / unit * unit;
-  if (cap < unit) cap = unit;
-  return K <= cap ? K : cap;
-}
+int sched_class(int N, int K, int ksplit) { return ksplit == 1 ? (N >= 131072) : (K > 4096); }
 
-int rows_per_block(int M, int ksplit) {
-  const int R = ksplit == 4 ? cfg_R(M, 4) : cfg_R(M, 1);
-  return (ksplit == 1 ? kWaves * kSlots : kSlots) * R;
+template <int R, int KSPLIT>
+constexpr int rows_per_block_of() { return (KSPLIT == 1 ? kWaves * kSlots : kSlots) * R; }
+
+template <int M>
+int rows_per_block(int ksplit, int cls) {
+  if (ksplit == 4) return cls ? rows_per_block_of<Sched<M, 4, 1>::R, 4>() : rows_per_block_of<Sched<M, 4, 0>::R, 4>();
+  return cls ? rows_per_block_of<Sched<M, 1, 1>::R, 1>() : rows_per_block_of<Sched<M, 1, 0>::R, 1>();
 }
 
 // ---------------------------------------------------------------------------
@@ -64,13 +70,13 @@ __device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first
     }
 }
 
-template <int M, int R, int U, int KSPLIT>
+template <int M, int R, int CPL, int KSPLIT>
 __global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __restrict__ x,
                                                              const uint32_t* __restrict__ qw,
                                                              const uint16_t* __restrict__ scales,
                                                              const uint16_t* __restrict__ biases, void* __restrict__ y,
-                                                             int out_f32, int N, int K, int kseg) {
-  extern __shared__ float4 xs[];
+                                                             int out_f32, int N, int K) {
+  __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kWaves * kSlots * R * M];
   using RM = RowMap<R, KSPLIT>;
   XRows<M> xr;
@@ -81,20 +87,20 @@ __global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __r
     yoff[m] = (size_t)m * N;
   }
   const RowSrc src{qw, scales, biases, N, K};
-  const int row_first = RM::first_row(blockIdx.x * RM::kRowsPerBlock);
+  const int block_row0 = blockIdx.x * RM::kRowsPerBlock;
   float acc[R][M];
-  block_rows<M, R, U, KSPLIT>(acc, xr, src, kseg, row_first, xs, red);
-  store_to<M, R, KSPLIT>(acc, row_first, N, y, yoff, out_f32 != 0);
+  block_rows<M, R, CPL, KSPLIT>(acc, xr, src, block_row0, xs, red);
+  store_to<M, R, KSPLIT>(acc, RM::first_row(block_row0), N, y, yoff, out_f32 != 0);
 }
 
-template <int M, int R, int U, int KSPLIT>
+template <int M, int R, int CPL, int KSPLIT>
 __global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint16_t* __restrict__ biases,
                                                               void* __restrict__ logits, int out_f32,
-                                                              uint64_t* __restrict__ partial, int N, int K, int kseg) {
-  extern __shared__ float4 xs[];
+                                                              uint64_t* __restrict__ partial, int N, int K) {
+  __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kWaves * kSlots * R * M];
   __shared__ uint64_t keys[kWaves * kSlots][M];
   using RM = RowMap<R, KSPLIT>;
@@ -106,9 +112,10 @@ __global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __
     yoff[m] = (size_t)m * N;
   }
   const RowSrc src{qw, scales, biases, N, K};
-  const int row_first = RM::first_row(blockIdx.x * RM::kRowsPerBlock);
+  const int block_row0 = blockIdx.x * RM::kRowsPerBlock;
+  const int row_first = RM::first_row(block_row0);
   float acc[R][M];
-  block_rows<M, R, U, KSPLIT>(acc, xr, src, kseg, row_first, xs, red);
+  block_rows<M, R, CPL, KSPLIT>(acc, xr, src, block_row0, xs, red);
   if (logits) store_to<M, R, KSPLIT>(acc, row_first, N, logits, yoff, out_f32 != 0);
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -160,10 +167,11 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __
 }
 
 // One pass of the routed product: C slots routed to one expert.
-template <int C, int R, int U, int KSPLIT>
+template <int C, int R, int CPL, int KSPLIT>
 __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, int x_per_slot, int top_k,
-                                            const RowSrc& src, int kseg, int row_first, void* y, bool out_f32,
-                                            float4* xs, float* red) {
+                                            const RowSrc& src, int block_row0, void* y, bool out_f32, float4* xs,
+                                            float* red) {
+  using RM = RowMap<R, KSPLIT>;
   XRows<C> xr;
   size_t yoff[C];
 #pragma unroll
@@ -173,19 +181,19 @@ __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, 
     yoff[i] = (size_t)sl * src.N;
   }
   float acc[R][C];
-  block_rows<C, R, U, KSPLIT>(acc, xr, src, kseg, row_first, xs, red);
-  store_to<C, R, KSPLIT>(acc, row_first, src.N, y, yoff, out_f32);
+  block_rows<C, R, CPL, KSPLIT>(acc, xr, src, block_row0, xs, red);
+  store_to<C, R, KSPLIT>(acc, RM::first_row(block_row0), src.N, y, yoff, out_f32);
 }
 
-template <int MB, int R, int U, int KSPLIT>
+template <int MB, int R, int CPL, int KSPLIT>
 __global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __restrict__ x, int x_per_slot,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint16_t* __restrict__ biases,
                                                               const int32_t* __restrict__ ids, void* __restrict__ y,
                                                               int out_f32, int M, int top_k, int E, int N, int K,
-                                                              int kseg, int tiles) {
-  extern __shared__ float4 xs[];
+                                                              int tiles) {
+  __shared__ float4 xs[MB * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kWaves * kSlots * R * MB];
   using RM = RowMap<R, KSPLIT>;
   const int nslots = M * top_k;
@@ -211,7 +219,6 @@ __global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __
   const size_t wpr = (size_t)(K >> 3);
   const size_t gpr = (size_t)(K >> 6);
   const RowSrc src{qw + (size_t)e * N * wpr, scales + (size_t)e * N * gpr, biases + (size_t)e * N * gpr, N, K};
-  const int row_first = RM::first_row(block_row0);
   int j = slot;
   while (j < nslots) {
     int list[MB];
@@ -220,14 +227,14 @@ __global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __
       if (ids[j] == e) list[cnt++] = j;
     if (cnt == 0) break;
     switch (cnt) {
-      case 1: routed_pass<1, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
-      case 2: if constexpr (MB >= 2) routed_pass<2, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
-      case 3: if constexpr (MB >= 3) routed_pass<3, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
-      case 4: if constexpr (MB >= 4) routed_pass<4, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
-      case 5: if constexpr (MB >= 5) routed_pass<5, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
-      case 6: if constexpr (MB >= 6) routed_pass<6, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
-      case 7: if constexpr (MB >= 7) routed_pass<7, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
-      default: if constexpr (MB >= 8) routed_pass<8, R, U, KSPLIT>(list, x, x_per_slot, top_k, src, kseg, row_first, y, out_f32, xs, red); break;
+      case 1: routed_pass<1, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 4: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 5: if constexpr (MB >= 5) routed_pass<5, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 6: if constexpr (MB >= 6) routed_pass<6, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 7: if constexpr (MB >= 7) routed_pass<7, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      default: if constexpr (MB >= 8) routed_pass<8, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
     }
   }
 }
@@ -294,51 +301,61 @@ w4a16_status_t check_shape(int M, int N, int K, int group, int out_dtype) {
 w4a16_status_t check_weights(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
                              const void* y, int out_dtype) {
   if (!x || !qw || !scales || !biases || !y) return W4A16_ERR_NULL;
-  if (!aligned(qw, 16) || !aligned(x, 4) || !aligned(scales, 2) || !aligned(biases, 2) ||
+  if (!aligned(qw, 16) || !aligned(x, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
       !aligned(y, out_dtype == W4A16_OUT_F32 ? 4 : 2))
     return W4A16_ERR_ALIGN;
   return W4A16_OK;
 }
 
-template <int M, int KSPLIT>
+template <int M, int R, int CPL, int KSPLIT>
+hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
+                              int out_f32, int N, int K, hipStream_t st) {
+  using RM = RowMap<R, KSPLIT>;
+  const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
+  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT>), dim3(blocks), dim3(kThreads), 0, st, x, qw, s, b, y,
+                     out_f32, N, K);
+  return hipGetLastError();
+}
+
+template <int M, int KSPLIT, int CLS>
 hipError_t launch_dense(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
                         int out_f32, int N, int K, hipStream_t st) {
-  constexpr int R = cfg_R(M, KSPLIT), U = cfg_U(M, KSPLIT);
-  using RM = RowMap<R, KSPLIT>;
-  const int kseg = kseg_for(M, K, KSPLIT);
-  const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
-  const size_t lds = (size_t)M * kseg * sizeof(float);
-  hipLaunchKernelGGL((qmm_dense_kernel<M, R, U, KSPLIT>), dim3(blocks), dim3(kThreads), lds, st, x, qw, s, b, y,
-                     out_f32, N, K, kseg);
-  return hipGetLastError();
+  using S = Sched<M, KSPLIT, CLS>;
+  return launch_dense_sched<M, S::R, S::CPL, KSPLIT>(x, qw, s, b, y, out_f32, N, K, st);
 }
 
 template <int M>
 hipError_t dense_by_split(int ksplit, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                           void* y, int out_f32, int N, int K, hipStream_t st) {
-  return ksplit == 4 ? launch_dense<M, 4>(x, qw, s, b, y, out_f32, N, K, st)
-                     : launch_dense<M, 1>(x, qw, s, b, y, out_f32, N, K, st);
+  const int cls = sched_class(N, K, ksplit);
+  if (ksplit == 4)
+    return cls ? launch_dense<M, 4, 1>(x, qw, s, b, y, out_f32, N, K, st)
+               : launch_dense<M, 4, 0>(x, qw, s, b, y, out_f32, N, K, st);
+  return cls ? launch_dense<M, 1, 1>(x, qw, s, b, y, out_f32, N, K, st)
+             : launch_dense<M, 1, 0>(x, qw, s, b, y, out_f32, N, K, st);
 }
 
-template <int M, int KSPLIT>
+template <int M, int KSPLIT, int CLS>
 hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* logits,
                          int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
-  constexpr int R = cfg_R(M, KSPLIT), U = cfg_U(M, KSPLIT);
-  using RM = RowMap<R, KSPLIT>;
-  const int kseg = kseg_for(M, K, KSPLIT);
+  using S = Sched<M, KSPLIT, CLS>;
+  using RM = RowMap<S::R, KSPLIT>;
   const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   *nblocks = blocks;
-  const size_t lds = (size_t)M * kseg * sizeof(float);
-  hipLaunchKernelGGL((qmm_lmhead_kernel<M, R, U, KSPLIT>), dim3(blocks), dim3(kThreads), lds, st, x, qw, s, b, logits,
-                     out_f32, partial, N, K, kseg);
+  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT>), dim3(blocks), dim3(kThreads), 0, st, x, qw, s, b,
+                     logits, out_f32, partial, N, K);
   return hipGetLastError();
 }
 
 template <int M>
 hipError_t lmhead_by_split(int ksplit, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                            void* logits, int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
-  return ksplit == 4 ? launch_lmhead<M, 4>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks)
-                     : launch_lmhead<M, 1>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks);
+  const int cls = sched_class(N, K, ksplit);
+  if (ksplit == 4)
+    return cls ? launch_lmhead<M, 4, 1>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks)
+               : launch_lmhead<M, 4, 0>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks);
+  return cls ? launch_lmhead<M, 1, 1>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks)
+             : launch_lmhead<M, 1, 0>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks);
 }
 
 // Routed kernels: MB = most slots one expert is processed with per pass.
@@ -346,15 +363,13 @@ template <int MB, int KSPLIT>
 hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                          const int32_t* ids, void* y, int out_f32, int M, int top_k, int E, int N, int K,
                          hipStream_t st) {
-  constexpr int R = cfg_R(MB, KSPLIT), U = cfg_U(MB, KSPLIT);
-  using RM = RowMap<R, KSPLIT>;
-  const int kseg = kseg_for(MB, K, KSPLIT);
+  using S = Sched<MB, KSPLIT, 0>;
+  using RM = RowMap<S::R, KSPLIT>;
   const int tiles = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   const size_t blocks = (size_t)tiles * M * top_k;
   if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
-  const size_t lds = (size_t)MB * kseg * sizeof(float);
-  hipLaunchKernelGGL((qmm_routed_kernel<MB, R, U, KSPLIT>), dim3((unsigned)blocks), dim3(kThreads), lds, st, x,
-                     x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, kseg, tiles);
+  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                     x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, tiles);
   return hipGetLastError();
 }
 
@@ -367,8 +382,31 @@ hipError_t routed_by_split(int ksplit, const uint16_t* x, int x_per_slot, const 
 }
 
 int lmhead_blocks(int M, int N, int K) {
-  const int rpb = rows_per_block(M, ksplit_for(N, K));
+  const int ks = ksplit_for(N, K);
+  const int cls = sched_class(N, K, ks);
+  int rpb = 0;
+  switch (M) {
+    case 1: rpb = rows_per_block<1>(ks, cls); break;
+    case 2: rpb = rows_per_block<2>(ks, cls); break;
+    case 3: rpb = rows_per_block<3>(ks, cls); break;
+    case 4: rpb = rows_per_block<4>(ks, cls); break;
+    case 5: rpb = rows_per_block<5>(ks, cls); break;
+    case 6: rpb = rows_per_block<6>(ks, cls); break;
+    case 7: rpb = rows_per_block<7>(ks, cls); break;
+    default: rpb = rows_per_block<8>(ks, cls); break;
+  }
   return (N + rpb - 1) / rpb;
+}
+
+template <int M>
+void sched_of(int ks, int cls, int* R, int* CPL) {
+  if (ks == 4) {
+    *R = cls ? Sched<M, 4, 1>::R : Sched<M, 4, 0>::R;
+    *CPL = cls ? Sched<M, 4, 1>::CPL : Sched<M, 4, 0>::CPL;
+  } else {
+    *R = cls ? Sched<M, 1, 1>::R : Sched<M, 1, 0>::R;
+    *CPL = cls ? Sched<M, 1, 1>::CPL : Sched<M, 1, 0>::CPL;
+  }
 }
 
 }  // namespace
@@ -376,6 +414,25 @@ int lmhead_blocks(int M, int N, int K) {
 extern "C" {
 
 int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_schedule_name(int M, int N, int K, int group) {
+  static thread_local char buf[96];
+  if (check_shape(M, N, K, group, W4A16_OUT_BF16) != W4A16_OK || M == 0 || N == 0) return "";
+  const int ks = ksplit_for(N, K), cls = sched_class(N, K, ks);
+  int R = 0, CPL = 0;
+  switch (M) {
+    case 1: sched_of<1>(ks, cls, &R, &CPL); break;
+    case 2: sched_of<2>(ks, cls, &R, &CPL); break;
+    case 3: sched_of<3>(ks, cls, &R, &CPL); break;
+    case 4: sched_of<4>(ks, cls, &R, &CPL); break;
+    case 5: sched_of<5>(ks, cls, &R, &CPL); break;
+    case 6: sched_of<6>(ks, cls, &R, &CPL); break;
+    case 7: sched_of<7>(ks, cls, &R, &CPL); break;
+    default: sched_of<8>(ks, cls, &R, &CPL); break;
+  }
+  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d>", M, R, CPL, ks);
+  return buf;
+}
 
 const char* w4a16_status_str(w4a16_status_t s) {
   switch (s) {
@@ -446,7 +503,7 @@ w4a16_status_t w4a16_lmhead_argmax(const uint16_t* x, const uint32_t* qw, const 
   if (st != W4A16_OK) return st;
   if (M == 0 || N == 0) return W4A16_OK;
   if (!x || !qw || !scales || !biases || !argmax) return W4A16_ERR_NULL;
-  if (!aligned(qw, 16) || !aligned(x, 4) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(argmax, 4) ||
+  if (!aligned(qw, 16) || !aligned(x, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(argmax, 4) ||
       (logits && !aligned(logits, out_dtype == W4A16_OUT_F32 ? 4 : 2)))
     return W4A16_ERR_ALIGN;
   const size_t need = w4a16_lmhead_argmax_workspace_bytes(M, N, K, group);

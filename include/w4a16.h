@@ -39,7 +39,7 @@
  *     nothing is launched and nothing is written.
  *   - Calls are re-entrant.  Outputs must not alias inputs.
  *   - Empty problems (M == 0 or N == 0) succeed without launching.
- *   - Alignment: qw 16 bytes; x 4 bytes; scales, biases 2 bytes; y 2 bytes
+ *   - Alignment: qw and x 16 bytes; scales, biases 2 bytes; y 2 bytes
  *     (bf16) or 4 bytes (fp32); ids, argmax 4 bytes; workspace 8 bytes.
  *   - Only group == 64 and 4-bit codes are supported.
  *   - Asynchronous device faults surface at the caller's next synchronization.
@@ -145,6 +145,15 @@ w4a16_status_t w4a16_pack(const uint8_t *codes, uint32_t *qw, int N, int K, void
 
 /* Static description of a status code (never NULL). */
 const char *w4a16_status_str(w4a16_status_t s);
+
+/*
+ * Name of the kernel instantiation w4a16_matmul launches for this shape, as
+ * profilers report it ("qmm_dense_kernel<M, R, CPL, KSPLIT>": activation rows,
+ * rows per lane, 16-byte chunks per lane per K-tile, waves sharing a row).
+ * "" when the arguments are invalid.  The string lives in thread-local storage
+ * and stays valid until the next call on the same thread.
+ */
+const char *w4a16_schedule_name(int M, int N, int K, int group);
 
 /* W4A16_ABI_VERSION of the loaded library. */
 int w4a16_abi_version(void);

@@ -68,6 +68,7 @@ def test_matmul_rejects_bad_arguments(L):
     assert mm(L, y=None) == ENULL
     assert mm(L, qw=A4) == EALIGN            # packed codes need 16-byte loads
     assert mm(L, x=A16 + 2) == EALIGN
+    assert mm(L, x=A4) == EALIGN              # activations are read 16 bytes at a time
     assert mm(L, s=A16 + 1) == EALIGN
     assert mm(L, y=A16 + 2, out=1) == EALIGN  # fp32 output needs 4 bytes
 

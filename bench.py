@@ -42,6 +42,17 @@ def step_bytes(M: int, layers: int) -> int:
     return layers * sum(call_bytes(M, *synthetic.PROJECTIONS[p]) for p in synthetic.LAYER_ORDER)
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "qmm_dense_decode_step_traffic.json")
+
+
+def launch_grid(kernel: str, N: int) -> int:
+    """Threads launched by the dense kernel named `kernel` for N rows: blocks of
+    256 threads holding 16 row groups (4 when four waves share a row) of R rows."""
+    M, R, CPL, KS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(","))
+    rows = (16 if KS == 1 else 4) * R
+    return -(-N // rows) * 256
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -211,8 +222,19 @@ def main():
     avg_us = pg["us_total"] / pg["launches"]
     avg_bytes = pg["bytes_total"] / pg["launches"]
     achieved = avg_bytes / (avg_us * 1e-6) / 1e9
+    # HBM bytes per launch from the committed counter record (null when the
+    # kernels changed after the counters were taken)
+    from decode_w4a16_affine_amd import profiling
+
+    weights = {}
+    for p in pg["projections"]:
+        N, K = synthetic.PROJECTIONS[p]
+        grid = launch_grid(dom, N)
+        weights[grid] = weights.get(grid, 0) + 1
+    traffic = profiling.traffic_per_launch(TRAFFIC_RECORD, dom, weights)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / PEAK_GBS, 4),
+                    traffic=None if traffic is None else int(traffic),
                     kernel=dom, serves=pg["projections"], avg_launch_us=round(avg_us, 3),
                     avg_launch_bytes=int(avg_bytes),
                     per_projection_us={p: round(v, 3) for p, v in dur.items()},

@@ -1,0 +1,123 @@
+"""Summaries of rocprofv3 output for the W4A16 kernels.
+
+Turns the CSV files of ``rocprofv3 --kernel-trace --stats`` and of two
+``rocprofv3 --pmc`` passes (FETCH_SIZE, then WRITE_SIZE) into short text
+summaries and a per-kernel traffic record.  Counter readings are converted to
+HBM bytes with the factor that a device-to-device copy of known size reads on
+the same counter (the benchmark's ``--calibrate-copy`` phase runs one).
+
+    python -m decode_w4a16_affine_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
+    python -m decode_w4a16_affine_amd.profiling traffic <fetch.csv> <write.csv> <out.json> "<fetch cmd>" "<write cmd>"
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", "qmm_device.hpp"), os.path.join(HERE, "csrc", "w4a16.hip")]
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_sha() -> str:
+    """Hash of the device code; counters taken on other code are stale."""
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"(qmm_\w+_kernel<[^>]*>|argmax_finalize_kernel|dequant_rows_kernel|pack_kernel)", name)
+    return m.group(1) if m else name.split("(")[0][:80]
+
+
+def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(path: str, counter: str):
+    out = []
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") == counter:
+            out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]) * 1024.0))
+    return out
+
+
+def _copy_factor(rows) -> float:
+    """Known bytes / counter bytes for the 256 MiB copy (the largest copy dispatch)."""
+    copies = [v for n, g, v in rows if "copyBuffer" in n]
+    big = sorted(copies, reverse=True)[:3]
+    if not big:
+        raise ValueError("no copy dispatch found for calibration")
+    return COPY_BYTES / statistics.median(big)
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, out_json: str, fetch_cmd: str, write_cmd: str) -> dict:
+    fr = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    wr = _per_dispatch(write_csv, "WRITE_SIZE")
+    ff, wf = _copy_factor(fr), _copy_factor(wr)
+    kernels = {}
+    for rows, key, fac in ((fr, "fetch_bytes", ff), (wr, "write_bytes", wf)):
+        groups = {}
+        for n, g, v in rows:
+            if "qmm_" not in n:
+                continue
+            groups.setdefault((short_name(n), g), []).append(v * fac)
+        for (k, g), vals in groups.items():
+            kernels.setdefault(k, {}).setdefault(str(g), {})[key] = statistics.median(vals)
+    rec = dict(source_sha256=kernel_source_sha(), copy_bytes=COPY_BYTES,
+               fetch_factor=round(ff, 5), write_factor=round(wf, 5),
+               fetch_command=fetch_cmd, write_command=write_cmd,
+               kernels={k: {g: dict(fetch_bytes=round(v.get("fetch_bytes", 0.0)),
+                                    write_bytes=round(v.get("write_bytes", 0.0)),
+                                    hbm_bytes=round(v.get("fetch_bytes", 0.0) + v.get("write_bytes", 0.0)))
+                            for g, v in sorted(d.items(), key=lambda kv: int(kv[0]))}
+                        for k, d in sorted(kernels.items())})
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def traffic_per_launch(record_path: str, kernel: str, grid_sizes_weights: dict):
+    """Average HBM bytes per launch of `kernel` over launches with the given grid
+    sizes (grid size -> launches per step), or None when the record is stale."""
+    if not os.path.exists(record_path):
+        return None
+    rec = json.load(open(record_path))
+    if rec.get("source_sha256") != kernel_source_sha():
+        return None
+    d = rec.get("kernels", {}).get(kernel)
+    if not d:
+        return None
+    tot = n = 0
+    for g, w in grid_sizes_weights.items():
+        if str(g) not in d:
+            return None
+        tot += d[str(g)]["hbm_bytes"] * w
+        n += w
+    return tot / n if n else None
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 2 and sys.argv[1] == "stats":
+        summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif len(sys.argv) >= 2 and sys.argv[1] == "traffic":
+        print(json.dumps(summarize_traffic(*sys.argv[2:7]), indent=1))
+    else:
+        print(__doc__)
+        sys.exit(2)

@@ -3,11 +3,15 @@
 A step is one decode token through the projections of a 42-layer,
 2560-hidden transformer (the Gemma-4 E4B shapes of the decode workload):
 per layer q, k, v, o (2560/512/512/2560 <- 2560), fused gate+up
-(20480 <- 2560) and down (2560 <- 10240), each a separate w4a16_matmul at
-M = 1, every layer with its own weights (2.2 GB in total, far beyond the
-256 MB last-level cache, so each call streams its weights from HBM).  The
+(20480 <- 2560) and down (2560 <- 10240) at M = 1, every layer with its own
+weights (2.2 GB in total, far beyond the 256 MB last-level cache, so each
+call streams its weights from HBM).  q, k and v read the same activations and
+are launched together (w4a16_matmul_grouped: separate matrices and outputs,
+bitwise the same results as separate calls); o, gate+up and down are single
+w4a16_matmul calls, as the data dependences of a decoder layer require.  The
 step is captured once in a HIP graph and replayed.  The same step at
-M = k+1 in {2, 3, 5} (speculative-verify batches) is reported alongside.
+M = k+1 in {2, 3, 5} (speculative-verify batches) and the step with six
+separate launches per layer are reported alongside.
 
 Prints ONE JSON line.  The value is whole-step throughput in algorithmic
 GB/s: packed codes + bf16 scales/biases + bf16 x + bf16 y per call.
@@ -86,18 +90,32 @@ def build_stack(torch, layers: int):
     return stack, host0
 
 
-def make_step(w4, stack, M: int, layers: int, only=None):
-    order = [p for p in synthetic.LAYER_ORDER if only is None or p in only]
-    xs = {p: stack[p]["x"][:M] for p in order}
-    ys = {p: stack[p]["y"][:M] for p in order}
+# Launch units of one layer: the projections in a unit share their activations
+# and go out in one call.
+UNITS_GROUPED = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate_up",)), ("down", ("down",)))
+UNITS_SEPARATE = tuple((p, (p,)) for p in synthetic.LAYER_ORDER)
+
+
+def make_step(w4, stack, M: int, layers: int, units=UNITS_GROUPED, only=None):
+    units = [u for u in units if only is None or u[0] in only]
+    xs = {u: stack[ps[0]]["x"][:M] for u, ps in units}
+    ys = {p: stack[p]["y"][:M] for _, ps in units for p in ps}
 
     def step():
         for l in range(layers):
-            for p in order:
-                d = stack[p]
-                w4.w4a16_matmul(xs[p], d["qw"][l], d["s"][l], d["b"][l], ys[p])
+            for u, ps in units:
+                if len(ps) == 1:
+                    d = stack[ps[0]]
+                    w4.w4a16_matmul(xs[u], d["qw"][l], d["s"][l], d["b"][l], ys[ps[0]])
+                else:
+                    w4.w4a16_matmul_grouped(xs[u], [(stack[p]["qw"][l], stack[p]["s"][l], stack[p]["b"][l], ys[p])
+                                                   for p in ps])
 
     return step
+
+
+def unit_bytes(M: int, ps) -> int:
+    return sum(call_bytes(M, *synthetic.PROJECTIONS[p]) for p in ps)
 
 
 def capture(torch, fn):
@@ -126,17 +144,20 @@ def time_graph(torch, g, steps: int, warmup: int) -> float:
 
 
 def kernel_durations(torch, w4, stack, layers: int, reps: int = 10):
-    """Average duration of one launch of each projection: a graph holding that
-    projection's launch for every layer (cold weights) is replayed `reps`
-    times between two events on the replay stream, and the elapsed time is
-    divided by the number of launches.  Graph replays leave no measurable
-    gap between consecutive kernels, so this is the kernel duration."""
+    """Average duration of one launch of each unit of the grouped step: a
+    graph holding that unit's launch for every layer (cold weights) is
+    replayed `reps` times between two events on the replay stream, and the
+    elapsed time is divided by the number of launches.  Graph replays leave no
+    measurable gap between consecutive kernels, so this is the kernel
+    duration."""
     out = {}
-    for p in synthetic.LAYER_ORDER:
-        g = capture(torch, make_step(w4, stack, 1, layers, only=(p,)))
-        out[p] = time_graph(torch, g, reps, 2) * 1e3 / layers
+    for u, ps in UNITS_GROUPED + tuple(x for x in UNITS_SEPARATE if x[0] in ("q", "k", "v")):
+        units = UNITS_GROUPED if u in dict(UNITS_GROUPED) else UNITS_SEPARATE
+        g = capture(torch, make_step(w4, stack, 1, layers, units=units, only=(u,)))
+        out[u] = time_graph(torch, g, reps, 2) * 1e3 / layers
         del g
     return out
+
 
 def cpu_baseline(host0, seconds: float = 10.0):
     """The oracle, as it stands, on one host core over layer 0's projections."""
@@ -204,19 +225,24 @@ def main():
         results[M] = dict(ms=ms, gbs=nb / (ms * 1e-3) / 1e9, bytes=nb, steps=steps, warmup=warm)
         log(f"M={M}: {ms:.4f} ms/step, {results[M]['gbs']:.1f} GB/s")
         del g
+    g = capture(torch, make_step(w4, stack, 1, L, units=UNITS_SEPARATE))
+    ms_sep = time_graph(torch, g, args.steps, args.warmup)
+    del g
+    log(f"M=1, six launches per layer: {ms_sep:.4f} ms/step")
 
     # Dominant kernel (largest share of the M=1 step): one kernel symbol per
-    # schedule, so projections are grouped by the kernel that serves them.
+    # schedule, so launch units are grouped by the kernel that serves them.
     dur = kernel_durations(torch, w4, stack, L)
-    groups = {}
-    for p in synthetic.LAYER_ORDER:
-        N, K = synthetic.PROJECTIONS[p]
-        groups.setdefault(w4.w4a16_schedule_name(1, N, K), []).append(p)
     per_group = {}
-    for name, ps in groups.items():
-        per_group[name] = dict(us_total=sum(dur[p] for p in ps),
-                               bytes_total=sum(call_bytes(1, *synthetic.PROJECTIONS[p]) for p in ps),
-                               launches=len(ps), projections=ps)
+    for u, ps in UNITS_GROUPED:
+        N, K = synthetic.PROJECTIONS[ps[0]]
+        kern = w4.w4a16_schedule_name(1, N, K)
+        e = per_group.setdefault(kern, dict(us_total=0.0, bytes_total=0, launches=0, units=[], grids=[]))
+        e["us_total"] += dur[u]
+        e["bytes_total"] += unit_bytes(1, ps)
+        e["launches"] += 1
+        e["units"].append(u)
+        e["grids"].append(sum(launch_grid(kern, synthetic.PROJECTIONS[p][0]) for p in ps))
     dom = max(per_group, key=lambda k: per_group[k]["us_total"])
     pg = per_group[dom]
     avg_us = pg["us_total"] / pg["launches"]
@@ -227,21 +253,20 @@ def main():
     from decode_w4a16_affine_amd import profiling
 
     weights = {}
-    for p in pg["projections"]:
-        N, K = synthetic.PROJECTIONS[p]
-        grid = launch_grid(dom, N)
+    for grid in pg["grids"]:
         weights[grid] = weights.get(grid, 0) + 1
     traffic = profiling.traffic_per_launch(TRAFFIC_RECORD, dom, weights)
+    unit_ps = dict(UNITS_GROUPED + UNITS_SEPARATE)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_GBS, 4),
                     traffic=None if traffic is None else int(traffic),
-                    kernel=dom, serves=pg["projections"], avg_launch_us=round(avg_us, 3),
+                    kernel=dom, serves=pg["units"], avg_launch_us=round(avg_us, 3),
                     avg_launch_bytes=int(avg_bytes),
-                    per_projection_us={p: round(v, 3) for p, v in dur.items()},
-                    per_projection_gbs={p: round(call_bytes(1, *synthetic.PROJECTIONS[p]) / (v * 1e-6) / 1e9, 1)
-                                        for p, v in dur.items()},
-                    per_projection_frac={p: round(call_bytes(1, *synthetic.PROJECTIONS[p]) / (v * 1e-6) / 1e9
-                                                  / PEAK_GBS, 4) for p, v in dur.items()})
+                    per_launch_us={u: round(v, 3) for u, v in dur.items()},
+                    per_launch_gbs={u: round(unit_bytes(1, unit_ps[u]) / (v * 1e-6) / 1e9, 1)
+                                    for u, v in dur.items()},
+                    per_launch_frac={u: round(unit_bytes(1, unit_ps[u]) / (v * 1e-6) / 1e9 / PEAK_GBS, 4)
+                                     for u, v in dur.items()})
 
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -272,9 +297,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"decode step, M=1: {L} layers x (q,k,v,o 2560/512/512/2560<-2560, "
-                               "gate_up 20480<-2560, down 2560<-10240), W4 group 64, bf16 x/y, "
-                               "one HIP graph per step",
-                   "layers": L, "bytes_per_step": r1["bytes"], "frac_of_peak": round(r1["gbs"] / PEAK_GBS, 4)},
+                               "gate_up 20480<-2560, down 2560<-10240), W4 group 64, bf16 x/y; "
+                               "q/k/v in one grouped launch, one HIP graph per step",
+                   "layers": L, "bytes_per_step": r1["bytes"], "frac_of_peak": round(r1["gbs"] / PEAK_GBS, 4),
+                   "six_launches_per_layer": dict(ms_per_step=round(ms_sep, 5),
+                                                  gbs=round(r1["bytes"] / (ms_sep * 1e-3) / 1e9, 2))},
         "verify": {str(M): dict(gbs=round(r["gbs"], 2), ms_per_step=round(r["ms"], 5),
                                 frac_of_peak=round(r["gbs"] / PEAK_GBS, 4),
                                 cost_vs_m1=round(r["ms"] / r1["ms"], 4))

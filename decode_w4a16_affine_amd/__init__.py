@@ -29,9 +29,15 @@ MAX_M = 8
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN",
           5: "ERR_WORKSPACE", 6: "ERR_HIP"}
 
-EXPORTS = ("w4a16_matmul", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
+EXPORTS = ("w4a16_matmul", "w4a16_matmul_grouped", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
            "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_pack", "w4a16_status_str",
            "w4a16_abi_version", "w4a16_schedule_name")
+
+
+class Matrix(ctypes.Structure):
+    """w4a16_matrix_t: one matrix of a grouped product."""
+    _fields_ = [("qw", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int)]
 
 
 class W4A16Error(RuntimeError):
@@ -55,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.w4a16_matmul.restype = _int
         L.w4a16_matmul.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]
+        L.w4a16_matmul_grouped.restype = _int
+        L.w4a16_matmul_grouped.argtypes = [_vp, ctypes.POINTER(Matrix), _int, _int, _int, _int, _int, _vp]
         L.w4a16_matmul_id.restype = _int
         L.w4a16_matmul_id.argtypes = [_vp, _int, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
                                       _int, _int, _vp]
@@ -127,6 +135,23 @@ def w4a16_matmul(x, qw, scales, biases, y, group: int = GROUP, stream=None) -> N
     N = qw.shape[0]
     _check(lib().w4a16_matmul(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(y), _out_code(y),
                               M, N, K, group, _stream(stream)), "w4a16_matmul")
+
+
+def w4a16_matmul_grouped(x, mats, group: int = GROUP, stream=None) -> None:
+    """mats: sequence of (qw, scales, biases, y) sharing K and x; y_i[M,N_i] = x . W_i^T."""
+    _dtype(x, torch.bfloat16, "x")
+    M, K = x.shape
+    arr = (Matrix * max(1, len(mats)))()
+    code = None
+    for i, (qw, s, b, y) in enumerate(mats):
+        _dtype(qw, torch.int32, "qw")
+        c = _out_code(y)
+        if code is not None and c != code:
+            raise TypeError("all outputs of a grouped product share one dtype")
+        code = c
+        arr[i] = Matrix(_ptr(qw), _ptr(s), _ptr(b), _ptr(y), qw.shape[0])
+    _check(lib().w4a16_matmul_grouped(_ptr(x), arr, len(mats), OUT_BF16 if code is None else code, M, K, group,
+                                      _stream(stream)), "w4a16_matmul_grouped")
 
 
 def w4a16_matmul_id(x, qw, scales, biases, ids, y, x_per_slot: bool = False, group: int = GROUP,

@@ -70,27 +70,47 @@ __device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first
     }
 }
 
+// Up to kMaxMats matrices that share K and the activations, launched together;
+// blocks [block0, next block0) of the grid stream matrix i.
+constexpr int kMaxMats = 8;
+struct MatDesc {
+  const uint32_t* qw;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  void* y;
+  int N;
+  int block0;
+};
+struct MatList {
+  MatDesc m[kMaxMats];
+  int count;
+};
+
 template <int M, int R, int CPL, int KSPLIT>
-__global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __restrict__ x,
-                                                             const uint32_t* __restrict__ qw,
-                                                             const uint16_t* __restrict__ scales,
-                                                             const uint16_t* __restrict__ biases, void* __restrict__ y,
-                                                             int out_f32, int N, int K) {
+__global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __restrict__ x, const MatList mats,
+                                                             int out_f32, int K) {
   __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kWaves * kSlots * R * M];
   using RM = RowMap<R, KSPLIT>;
+  // this block's matrix: a uniform scan with static indices (no dynamic
+  // indexing of the argument block)
+  const int b = blockIdx.x;
+  MatDesc d = mats.m[0];
+#pragma unroll
+  for (int i = 1; i < kMaxMats; ++i)
+    if (i < mats.count && b >= mats.m[i].block0) d = mats.m[i];
   XRows<M> xr;
   size_t yoff[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     xr.p[m] = x + (size_t)m * K;
-    yoff[m] = (size_t)m * N;
+    yoff[m] = (size_t)m * d.N;
   }
-  const RowSrc src{qw, scales, biases, N, K};
-  const int block_row0 = blockIdx.x * RM::kRowsPerBlock;
+  const RowSrc src{d.qw, d.scales, d.biases, d.N, K};
+  const int block_row0 = (b - d.block0) * RM::kRowsPerBlock;
   float acc[R][M];
   block_rows<M, R, CPL, KSPLIT>(acc, xr, src, block_row0, xs, red);
-  store_to<M, R, KSPLIT>(acc, RM::first_row(block_row0), N, y, yoff, out_f32 != 0);
+  store_to<M, R, KSPLIT>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
 }
 
 template <int M, int R, int CPL, int KSPLIT>
@@ -308,31 +328,58 @@ w4a16_status_t check_weights(const uint16_t* x, const uint32_t* qw, const uint16
 }
 
 template <int M, int R, int CPL, int KSPLIT>
-hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
-                              int out_f32, int N, int K, hipStream_t st) {
+hipError_t launch_dense_list(const uint16_t* x, MatList ml, int out_f32, int K, hipStream_t st) {
   using RM = RowMap<R, KSPLIT>;
-  const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
-  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT>), dim3(blocks), dim3(kThreads), 0, st, x, qw, s, b, y,
-                     out_f32, N, K);
+  long blocks = 0;
+  for (int i = 0; i < ml.count; ++i) {
+    ml.m[i].block0 = (int)blocks;
+    blocks += (ml.m[i].N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
+  }
+  if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT>), dim3((unsigned)blocks), dim3(kThreads), 0, st, x, ml,
+                     out_f32, K);
   return hipGetLastError();
 }
 
-template <int M, int KSPLIT, int CLS>
-hipError_t launch_dense(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
-                        int out_f32, int N, int K, hipStream_t st) {
-  using S = Sched<M, KSPLIT, CLS>;
-  return launch_dense_sched<M, S::R, S::CPL, KSPLIT>(x, qw, s, b, y, out_f32, N, K, st);
+template <int M, int R, int CPL, int KSPLIT>
+hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
+                              int out_f32, int N, int K, hipStream_t st) {
+  MatList ml{};
+  ml.m[0] = MatDesc{qw, s, b, y, N, 0};
+  ml.count = 1;
+  return launch_dense_list<M, R, CPL, KSPLIT>(x, ml, out_f32, K, st);
 }
 
+template <int M, int KSPLIT, int CLS>
+hipError_t launch_dense(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
+  using S = Sched<M, KSPLIT, CLS>;
+  return launch_dense_list<M, S::R, S::CPL, KSPLIT>(x, ml, out_f32, K, st);
+}
+
+// Every matrix of `ml` must have the K-split `ksplit`; the schedule class
+// follows the tallest matrix (the class never changes a row's arithmetic).
 template <int M>
-hipError_t dense_by_split(int ksplit, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
-                          void* y, int out_f32, int N, int K, hipStream_t st) {
-  const int cls = sched_class(N, K, ksplit);
+hipError_t dense_by_split(int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
+  int nmax = 0;
+  for (int i = 0; i < ml.count; ++i) nmax = ml.m[i].N > nmax ? ml.m[i].N : nmax;
+  const int cls = sched_class(nmax, K, ksplit);
   if (ksplit == 4)
-    return cls ? launch_dense<M, 4, 1>(x, qw, s, b, y, out_f32, N, K, st)
-               : launch_dense<M, 4, 0>(x, qw, s, b, y, out_f32, N, K, st);
-  return cls ? launch_dense<M, 1, 1>(x, qw, s, b, y, out_f32, N, K, st)
-             : launch_dense<M, 1, 0>(x, qw, s, b, y, out_f32, N, K, st);
+    return cls ? launch_dense<M, 4, 1>(x, ml, out_f32, K, st) : launch_dense<M, 4, 0>(x, ml, out_f32, K, st);
+  return cls ? launch_dense<M, 1, 1>(x, ml, out_f32, K, st) : launch_dense<M, 1, 0>(x, ml, out_f32, K, st);
+}
+
+hipError_t dense_dispatch(int M, int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K,
+                          hipStream_t st) {
+  switch (M) {
+    case 1: return dense_by_split<1>(ksplit, x, ml, out_f32, K, st);
+    case 2: return dense_by_split<2>(ksplit, x, ml, out_f32, K, st);
+    case 3: return dense_by_split<3>(ksplit, x, ml, out_f32, K, st);
+    case 4: return dense_by_split<4>(ksplit, x, ml, out_f32, K, st);
+    case 5: return dense_by_split<5>(ksplit, x, ml, out_f32, K, st);
+    case 6: return dense_by_split<6>(ksplit, x, ml, out_f32, K, st);
+    case 7: return dense_by_split<7>(ksplit, x, ml, out_f32, K, st);
+    default: return dense_by_split<8>(ksplit, x, ml, out_f32, K, st);
+  }
 }
 
 template <int M, int KSPLIT, int CLS>
@@ -454,19 +501,42 @@ w4a16_status_t w4a16_matmul(const uint16_t* x, const uint32_t* qw, const uint16_
   if (M == 0 || N == 0) return W4A16_OK;
   st = check_weights(x, qw, scales, biases, y, out_dtype);
   if (st != W4A16_OK) return st;
-  const int f32 = out_dtype == W4A16_OUT_F32;
-  const int ks = ksplit_for(N, K);
-  hipStream_t s = (hipStream_t)stream;
-  switch (M) {
-    case 1: return launched(dense_by_split<1>(ks, x, qw, scales, biases, y, f32, N, K, s));
-    case 2: return launched(dense_by_split<2>(ks, x, qw, scales, biases, y, f32, N, K, s));
-    case 3: return launched(dense_by_split<3>(ks, x, qw, scales, biases, y, f32, N, K, s));
-    case 4: return launched(dense_by_split<4>(ks, x, qw, scales, biases, y, f32, N, K, s));
-    case 5: return launched(dense_by_split<5>(ks, x, qw, scales, biases, y, f32, N, K, s));
-    case 6: return launched(dense_by_split<6>(ks, x, qw, scales, biases, y, f32, N, K, s));
-    case 7: return launched(dense_by_split<7>(ks, x, qw, scales, biases, y, f32, N, K, s));
-    default: return launched(dense_by_split<8>(ks, x, qw, scales, biases, y, f32, N, K, s));
+  MatList ml{};
+  ml.m[0] = MatDesc{qw, scales, biases, y, N, 0};
+  ml.count = 1;
+  return launched(dense_dispatch(M, ksplit_for(N, K), x, ml, out_dtype == W4A16_OUT_F32, K, (hipStream_t)stream));
+}
+
+w4a16_status_t w4a16_matmul_grouped(const uint16_t* x, const w4a16_matrix_t* mats, int count, int out_dtype, int M,
+                                    int K, int group, void* stream) {
+  if (count < 0 || count > W4A16_MAX_GROUP) return W4A16_ERR_SHAPE;
+  if (count > 0 && !mats) return W4A16_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    w4a16_status_t st = check_shape(M, mats[i].N, K, group, out_dtype);
+    if (st != W4A16_OK) return st;
   }
+  if (count == 0) {
+    w4a16_status_t st = check_shape(M, 0, K, group, out_dtype);
+    return st;
+  }
+  if (M == 0) return W4A16_OK;
+  for (int i = 0; i < count; ++i) {
+    if (mats[i].N == 0) continue;
+    w4a16_status_t st = check_weights(x, mats[i].qw, mats[i].scales, mats[i].biases, mats[i].y, out_dtype);
+    if (st != W4A16_OK) return st;
+  }
+  // one launch per K-split class (all matrices of a decode layer's q/k/v share one)
+  for (int ks : {4, 1}) {
+    MatList ml{};
+    ml.count = 0;
+    for (int i = 0; i < count; ++i)
+      if (mats[i].N > 0 && ksplit_for(mats[i].N, K) == ks)
+        ml.m[ml.count++] = MatDesc{mats[i].qw, mats[i].scales, mats[i].biases, mats[i].y, mats[i].N, 0};
+    if (ml.count == 0) continue;
+    const hipError_t e = dense_dispatch(M, ks, x, ml, out_dtype == W4A16_OUT_F32, K, (hipStream_t)stream);
+    if (e != hipSuccess) return W4A16_ERR_HIP;
+  }
+  return W4A16_OK;
 }
 
 w4a16_status_t w4a16_matmul_id(const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* scales,

@@ -56,6 +56,7 @@ extern "C" {
 
 #define W4A16_ABI_VERSION 1
 #define W4A16_MAX_M 8
+#define W4A16_MAX_GROUP 8
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
@@ -82,6 +83,31 @@ typedef enum w4a16_out {
 w4a16_status_t w4a16_matmul(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
                             const uint16_t *biases, void *y, int out_dtype, int M, int N, int K,
                             int group, void *stream);
+
+/*
+ * One matrix of a grouped product: packed weights, scales, biases and its
+ * output y [M][N] (bf16 or fp32 per the call's out_dtype).
+ */
+typedef struct w4a16_matrix {
+    const uint32_t *qw;        /* [N][K/8] */
+    const uint16_t *scales;    /* [N][K/64] */
+    const uint16_t *biases;    /* [N][K/64] */
+    void *y;                   /* [M][N] */
+    int N;
+} w4a16_matrix_t;
+
+/*
+ * Grouped product: `count` (<= W4A16_MAX_GROUP) matrices with the same K that
+ * multiply the same activations x [M][K], computed in as few launches as the
+ * row schedule allows (one for the q, k and v projections of a decode layer).
+ * Each output is bitwise equal to a w4a16_matmul call on that matrix alone.
+ * This is the fused q/k/v launch the Gemma-4 megakernel page motivates (one
+ * launch instead of several for small decode projections, "What it does").
+ * `mats` is a HOST array read during the call; every pointer in it is device
+ * memory with the alignment of w4a16_matmul.  Matrices with N == 0 are skipped.
+ */
+w4a16_status_t w4a16_matmul_grouped(const uint16_t *x, const w4a16_matrix_t *mats, int count,
+                                    int out_dtype, int M, int K, int group, void *stream);
 
 /*
  * Routed (expert-gathered) product for MoE decode: the routed-expert matvec

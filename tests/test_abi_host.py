@@ -94,6 +94,33 @@ def test_matmul_id_rejects_bad_arguments(L):
     assert mid(M=0, ids=None) == OK
 
 
+def test_grouped_rejects_bad_arguments(L):
+    arr = (w4.Matrix * 3)()
+    for i in range(3):
+        arr[i] = w4.Matrix(A16, A16, A16, A16, 64)
+
+    def gr(count=3, M=1, K=128, group=64, out=0, x=A16):
+        return L.w4a16_matmul_grouped(x, arr, count, out, M, K, group, None)
+
+    assert gr(count=9) == ESHAPE
+    assert gr(count=-1) == ESHAPE
+    assert gr(K=100) == ESHAPE
+    assert gr(group=32) == EUNSUP
+    assert gr(M=9) == EUNSUP
+    assert gr(x=None) == ENULL
+    assert gr(x=A16 + 8) == EALIGN
+    arr[1] = w4.Matrix(A4, A16, A16, A16, 64)
+    assert gr() == EALIGN
+    arr[1] = w4.Matrix(A16, None, A16, A16, 64)
+    assert gr() == ENULL
+    arr[1] = w4.Matrix(A16, A16, A16, A16, -2)
+    assert gr() == ESHAPE
+    assert L.w4a16_matmul_grouped(A16, None, 2, 0, 1, 128, 64, None) == ENULL
+    arr[1] = w4.Matrix(A16, A16, A16, A16, 64)
+    assert gr(count=0) == OK
+    assert gr(M=0) == OK
+
+
 def test_lmhead_workspace_rules(L):
     ws = L.w4a16_lmhead_argmax_workspace_bytes
     assert ws(1, 262144, 2560, 64) > 0

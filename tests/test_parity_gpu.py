@@ -229,6 +229,35 @@ def test_closed_forms_on_gpu(orc):
         full_check(orc, w, x, y64, absy, f"codes={c}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_grouped_equals_separate_calls(orc, M):
+    # the q, k, v projections of a decode layer in one grouped call, plus a wide
+    # matrix in another K-split class and an empty one
+    shapes = [("q", 2560), ("k", 512), ("v", 512), ("wide", 5000), ("empty", 0)]
+    K = 2560
+    x = synthetic.activations(M, K, seed=51)
+    xd = dev_bf16(x)
+    mats, outs, ws = [], [], []
+    for i, (name, N) in enumerate(shapes):
+        w = synthetic.quantized_weights(max(N, 1), K, seed=51, tag=(i,))
+        dw = DevWeights(w)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        mats.append((dw.qw[:N], dw.s[:N], dw.b[:N], y))
+        outs.append(y)
+        ws.append((w, dw))
+    say(f"grouped q/k/v/wide/empty M={M}")
+    w4.w4a16_matmul_grouped(xd, mats)
+    torch.cuda.synchronize()
+    for (name, N), y, (w, dw) in zip(shapes, outs, ws):
+        if N == 0:
+            continue
+        ref = run_mm(dw, x, N, f32=True)
+        assert np.array_equal(host_f32(y).view(np.uint32), ref.view(np.uint32)), name
+        rows = np.arange(0, N, 7, dtype=np.int32)
+        y64, absy = orc.qmm(x, w.qw, w.scales, w.biases, rows=rows)
+        check_f32(host_f32(y)[:, rows], y64, absy, f"grouped {name} M={M}")
+
+
 def test_deterministic_and_no_stray_writes(orc):
     N, K, M = 5000, 2560, 3
     say(f"determinism and guard bands N={N} K={K} M={M}")

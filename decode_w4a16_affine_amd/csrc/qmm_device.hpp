@@ -133,9 +133,9 @@ struct Tile {
   uint32_t b[CPL][R];
 };
 
-template <int M, int R, bool FAST>
+template <int M, int R, int CS, bool FAST>
 __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R], const float (&s)[R],
-                                          const float (&b)[R], const float4* xc, int cseg) {
+                                          const float (&b)[R], const float4* xc) {
   float s24[R], s20[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -147,8 +147,8 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
     float xv[M][8];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float4 lo = xc[(m * 8 + 2 * wd) * cseg];
-      const float4 hi = xc[(m * 8 + 2 * wd + 1) * cseg];
+      const float4 lo = xc[(m * 8 + 2 * wd) * CS];
+      const float4 hi = xc[(m * 8 + 2 * wd + 1) * CS];
       xv[m][0] = lo.x; xv[m][1] = lo.y; xv[m][2] = lo.z; xv[m][3] = lo.w;
       xv[m][4] = hi.x; xv[m][5] = hi.y; xv[m][6] = hi.z; xv[m][7] = hi.w;
     }
@@ -187,7 +187,8 @@ template <int M, int R, int CPL, int KSPLIT>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
-  constexpr int KTILE = CPL * LPR * 32;                       // codes per K-tile
+  constexpr int CS = CPL * LPR;                               // chunks per K-tile
+  constexpr int KTILE = CS * 32;                              // codes per K-tile
   constexpr int XL = (KTILE / 8 + kThreads - 1) / kThreads;   // 16-byte x loads per thread per row
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -245,9 +246,10 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
       }
     }
 
-    // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * cseg + c]
-    //    holds k = k0 + 32c + 4 piece .. +3, so lanes reading consecutive chunks
-    //    of one piece touch consecutive 16-byte words.
+    // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * CS + c]
+    //    holds k = k0 + 32c + 4 piece .. +3 (CS = chunks per K-tile, a
+    //    compile-time stride, so every read offset is an immediate), and lanes
+    //    reading consecutive chunks of one piece touch consecutive 16-byte words.
     __syncthreads();  // every wave is done with the previous contents of xs
     // Threads past the end repeat the last piece (same value, same address).
 #pragma unroll
@@ -258,8 +260,8 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
         const int kk = 8 * i;
         const int c = kk >> 5, piece = (kk >> 2) & 7;
         const uint4 v = xv[m][j];
-        xs[(m * 8 + piece) * cseg + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-        xs[(m * 8 + piece + 1) * cseg + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+        xs[(m * 8 + piece) * CS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+        xs[(m * 8 + piece + 1) * CS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
       }
     __syncthreads();
 
@@ -277,9 +279,9 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
           plain |= needs_plain(s[r]);
         }
         if (__any(plain))
-          chunk_fma<M, R, false>(acc, tl.w[j], s, b, xs + c, cseg);
+          chunk_fma<M, R, CS, false>(acc, tl.w[j], s, b, xs + c);
         else
-          chunk_fma<M, R, true>(acc, tl.w[j], s, b, xs + c, cseg);
+          chunk_fma<M, R, CS, true>(acc, tl.w[j], s, b, xs + c);
       }
     }
   }

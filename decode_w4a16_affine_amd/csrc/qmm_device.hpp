@@ -169,6 +169,104 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
   }
 }
 
+// Per-wave view of the rows being streamed: buffer resources that end at the
+// last real row (loads of rows >= N return zero), words and groups per row,
+// and this lane's place in the row (L) and in the wave (slot).
+struct WaveRows {
+  __amdgpu_buffer_rsrc_t rq, rs, rb;
+  uint32_t wpr;   // code words per row
+  uint32_t gpr;   // groups per row
+  int L;          // lane index within the row's LPR lanes
+  int slot;       // row group within the wave
+};
+
+// One K-tile [k0, k0 + klen) of the R rows of this lane's row group.
+// FULL: klen equals the tile size, so every chunk slot of every lane is in
+// range and all offsets are compile-time steps from one base per row (they
+// fold into the load instructions' immediate fields); otherwise chunk slots
+// past the end of the tile load nothing (offset outside the resource) and are
+// skipped.
+template <int M, int R, int CPL, int KSPLIT, bool FULL>
+__device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
+                                          int klen, float4* xs) {
+  constexpr int LPR = kRowLanes * KSPLIT;
+  constexpr int CS = CPL * LPR;                               // chunks per K-tile
+  constexpr int KTILE = CS * 32;                              // codes per K-tile
+  constexpr int XL = (KTILE / 8 + kThreads - 1) / kThreads;   // 16-byte x loads per thread per row
+  const int cseg = FULL ? CS : klen >> 5;    // chunks in this tile
+  const int cbase = k0 >> 5;
+  const int xq = FULL ? KTILE / 8 : klen >> 3;  // 16-byte x pieces per row in this tile
+  const int L = w.L;
+
+  // 1. activations of this tile (clamped indices: no branches around loads)
+  uint4 xv[M][XL];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+      xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + k0)[i];
+    }
+
+  // 2. every weight load of the tile
+  Tile<CPL, R> tl;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t lr = (uint32_t)(w.slot * R + r);
+    const uint32_t qb = lr * w.wpr * 4u + (uint32_t)(cbase + L) * 16u;   // byte offset of chunk slot 0
+    const uint32_t gb = lr * w.gpr * 2u + (uint32_t)((cbase + L) >> 1) * 2u;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      // chunk c = L + j*LPR; LPR is even, so its group is ((cbase + L) >> 1) + j*LPR/2
+      const bool ok = FULL || L + j * LPR < cseg;
+      const uint32_t oq = ok ? qb + (uint32_t)(j * LPR * 16) : kOffNone;
+      const uint32_t og = ok ? gb + (uint32_t)(j * LPR) : kOffNone;
+      tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, 0));
+      tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
+      tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
+    }
+  }
+
+  // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * CS + c]
+  //    holds k = k0 + 32c + 4 piece .. +3 (CS = chunks per K-tile, a
+  //    compile-time stride, so every read offset is an immediate), and lanes
+  //    reading consecutive chunks of one piece touch consecutive 16-byte words.
+  __syncthreads();  // every wave is done with the previous contents of xs
+  // Threads past the end repeat the last piece (same value, same address).
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+      const int kk = 8 * i;
+      const int c = kk >> 5, piece = (kk >> 2) & 7;
+      const uint4 v = xv[m][j];
+      xs[(m * 8 + piece) * CS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+      xs[(m * 8 + piece + 1) * CS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+    }
+  __syncthreads();
+
+  // 4. consume the chunks in ascending order
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = L + j * LPR;
+    if (FULL || c < cseg) {
+      float s[R], b[R];
+      bool plain = false;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        s[r] = __uint_as_float(tl.s[j][r] << 16);
+        b[r] = __uint_as_float(tl.b[j][r] << 16);
+        plain |= needs_plain(s[r]);
+      }
+      if (__any(plain))
+        chunk_fma<M, R, CS, false>(acc, tl.w[j], s, b, xs + c);
+      else
+        chunk_fma<M, R, CS, true>(acc, tl.w[j], s, b, xs + c);
+    }
+  }
+}
+
 // Full-row sums for the R rows of this lane's row group.
 //
 // Lane L of a row (L = t for KSPLIT 1, wave*16 + t for KSPLIT 4) owns the
@@ -187,25 +285,24 @@ template <int M, int R, int CPL, int KSPLIT>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
-  constexpr int CS = CPL * LPR;                               // chunks per K-tile
-  constexpr int KTILE = CS * 32;                              // codes per K-tile
-  constexpr int XL = (KTILE / 8 + kThreads - 1) / kThreads;   // 16-byte x loads per thread per row
+  constexpr int KTILE = CPL * LPR * 32;                       // codes per K-tile
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = lane & (kRowLanes - 1);
   const int slot = lane / kRowLanes;
-  const int L = KSPLIT == 1 ? t : wave * kRowLanes + t;
   const int K = src.K;
-  const uint32_t wpr = (uint32_t)(K >> 3);     // code words per row
-  const uint32_t gpr = (uint32_t)(K >> 6);     // groups per row
+  WaveRows w;
+  w.wpr = (uint32_t)(K >> 3);
+  w.gpr = (uint32_t)(K >> 6);
+  w.L = KSPLIT == 1 ? t : wave * kRowLanes + t;
+  w.slot = slot;
 
-  // Rows of this wave: [wave_row0, wave_row0 + kSlots*R); the resources end
-  // at the last real row, so loads of rows >= N return zero.
+  // Rows of this wave: [wave_row0, wave_row0 + kSlots*R).
   const int wave_row0 = block_row0 + (KSPLIT == 1 ? wave * kSlots * R : 0);
   const int nrows = max(0, min(kSlots * R, src.N - wave_row0));
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(src.qw + (size_t)wave_row0 * wpr, (uint32_t)nrows * wpr * 4u);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.scales + (size_t)wave_row0 * gpr, (uint32_t)nrows * gpr * 2u);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(src.biases + (size_t)wave_row0 * gpr, (uint32_t)nrows * gpr * 2u);
+  w.rq = make_rsrc(src.qw + (size_t)wave_row0 * w.wpr, (uint32_t)nrows * w.wpr * 4u);
+  w.rs = make_rsrc(src.scales + (size_t)wave_row0 * w.gpr, (uint32_t)nrows * w.gpr * 2u);
+  w.rb = make_rsrc(src.biases + (size_t)wave_row0 * w.gpr, (uint32_t)nrows * w.gpr * 2u);
 
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -214,76 +311,10 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
 
   for (int k0 = 0; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
-    const int cseg = klen >> 5;
-    const int cbase = k0 >> 5;
-    const int xq = klen >> 3;                  // 16-byte x pieces per row in this tile
-
-    // 1. activations of this tile (clamped indices: no branches around loads)
-    uint4 xv[M][XL];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int j = 0; j < XL; ++j) {
-        const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
-        xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + k0)[i];
-      }
-
-    // 2. every weight load of the tile
-    Tile<CPL, R> tl;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = L + j * LPR;
-      const bool ok = c < cseg;
-      const uint32_t cg = (uint32_t)(cbase + c);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t lr = (uint32_t)(slot * R + r);
-        const uint32_t oq = ok ? (lr * wpr + cg * 4u) * 4u : kOffNone;
-        const uint32_t og = ok ? (lr * gpr + (cg >> 1)) * 2u : kOffNone;
-        tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, oq, 0, 0));
-        tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, og, 0, 0);
-        tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(rb, og, 0, 0);
-      }
-    }
-
-    // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * CS + c]
-    //    holds k = k0 + 32c + 4 piece .. +3 (CS = chunks per K-tile, a
-    //    compile-time stride, so every read offset is an immediate), and lanes
-    //    reading consecutive chunks of one piece touch consecutive 16-byte words.
-    __syncthreads();  // every wave is done with the previous contents of xs
-    // Threads past the end repeat the last piece (same value, same address).
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int j = 0; j < XL; ++j) {
-        const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
-        const int kk = 8 * i;
-        const int c = kk >> 5, piece = (kk >> 2) & 7;
-        const uint4 v = xv[m][j];
-        xs[(m * 8 + piece) * CS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-        xs[(m * 8 + piece + 1) * CS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
-      }
-    __syncthreads();
-
-    // 4. consume the chunks in ascending order
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = L + j * LPR;
-      if (c < cseg) {
-        float s[R], b[R];
-        bool plain = false;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          s[r] = __uint_as_float(tl.s[j][r] << 16);
-          b[r] = __uint_as_float(tl.b[j][r] << 16);
-          plain |= needs_plain(s[r]);
-        }
-        if (__any(plain))
-          chunk_fma<M, R, CS, false>(acc, tl.w[j], s, b, xs + c);
-        else
-          chunk_fma<M, R, CS, true>(acc, tl.w[j], s, b, xs + c);
-      }
-    }
+    if (klen == KTILE)
+      tile_pass<M, R, CPL, KSPLIT, true>(acc, xr, w, k0, klen, xs);
+    else
+      tile_pass<M, R, CPL, KSPLIT, false>(acc, xr, w, k0, klen, xs);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -304,7 +335,7 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
       for (int m = 0; m < M; ++m) {
         float v = red[((0 * kSlots + slot) * R + r) * M + m];
 #pragma unroll
-        for (int w = 1; w < KSPLIT; ++w) v += red[((w * kSlots + slot) * R + r) * M + m];
+        for (int w2 = 1; w2 < KSPLIT; ++w2) v += red[((w2 * kSlots + slot) * R + r) * M + m];
         acc[r][m] = v;
       }
   }

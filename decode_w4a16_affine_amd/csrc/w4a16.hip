@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <type_traits>
+
 #include "qmm_device.hpp"
 #include "w4a16.h"
 
@@ -23,26 +25,48 @@ constexpr int kNarrowN = 4096;
 
 int ksplit_for(int N, int /*K*/) { return N <= kNarrowN ? 4 : 1; }
 
-// Schedules measured on MI355X (cold weights, back-to-back launches).  Class 0:
-// the default; class 1: very tall matrices (N >= 131072, vocabulary heads),
-// where two rows per lane win for KSPLIT 1, and long rows (K > 4096) for
-// KSPLIT 4, where a whole row fits one K-tile.
+// Schedules measured on MI355X (cold weights, graph-replayed launches).
+//
+// KSPLIT 1 classes (bit 0: very tall matrices, N >= 131072, vocabulary heads,
+// where two rows per lane win; bit 1: K a multiple of 2560 but not of 2048, so
+// tiles of 5 chunks per lane cover K exactly, otherwise 4): tiles that cover K
+// exactly use straight-line loads with immediate offsets.
+// KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile.
 template <int M, int KSPLIT, int CLS>
 struct Sched {
-  static constexpr int R = KSPLIT == 1 ? (CLS == 1 && M <= 5 ? 2 : 1) : 1;
-  static constexpr int CPL = KSPLIT == 1 ? (M == 1 ? (CLS == 1 ? 5 : 8) : M <= 3 ? 5 : 3)
+  static constexpr int R = KSPLIT == 1 ? ((CLS & 1) && M <= 5 ? 2 : 1) : 1;
+  static constexpr int CPL = KSPLIT == 1 ? (M <= 3 ? ((CLS & 2) ? 5 : 4) : 3)
                                          : (M <= 3 ? (CLS == 1 && M == 1 ? 5 : 2) : 1);
 };
 
-int sched_class(int N, int K, int ksplit) { return ksplit == 1 ? (N >= 131072) : (K > 4096); }
+int sched_class(int N, int K, int ksplit) {
+  if (ksplit == 4) return K > 4096;
+  return (N >= 131072 ? 1 : 0) | (K % 2048 != 0 && K % 2560 == 0 ? 2 : 0);
+}
+
+// Calls f(integral_constant<KSPLIT>, integral_constant<CLS>) for a runtime (ksplit, cls).
+template <typename F>
+auto with_sched(int ksplit, int cls, F&& f) {
+  using std::integral_constant;
+  if (ksplit == 4)
+    return cls ? f(integral_constant<int, 4>{}, integral_constant<int, 1>{})
+               : f(integral_constant<int, 4>{}, integral_constant<int, 0>{});
+  switch (cls) {
+    case 1: return f(integral_constant<int, 1>{}, integral_constant<int, 1>{});
+    case 2: return f(integral_constant<int, 1>{}, integral_constant<int, 2>{});
+    case 3: return f(integral_constant<int, 1>{}, integral_constant<int, 3>{});
+    default: return f(integral_constant<int, 1>{}, integral_constant<int, 0>{});
+  }
+}
 
 template <int R, int KSPLIT>
 constexpr int rows_per_block_of() { return (KSPLIT == 1 ? kWaves * kSlots : kSlots) * R; }
 
 template <int M>
 int rows_per_block(int ksplit, int cls) {
-  if (ksplit == 4) return cls ? rows_per_block_of<Sched<M, 4, 1>::R, 4>() : rows_per_block_of<Sched<M, 4, 0>::R, 4>();
-  return cls ? rows_per_block_of<Sched<M, 1, 1>::R, 1>() : rows_per_block_of<Sched<M, 1, 0>::R, 1>();
+  return with_sched(ksplit, cls, [](auto ks, auto c) {
+    return rows_per_block_of<Sched<M, decltype(ks)::value, decltype(c)::value>::R, decltype(ks)::value>();
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -362,10 +386,9 @@ template <int M>
 hipError_t dense_by_split(int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   int nmax = 0;
   for (int i = 0; i < ml.count; ++i) nmax = ml.m[i].N > nmax ? ml.m[i].N : nmax;
-  const int cls = sched_class(nmax, K, ksplit);
-  if (ksplit == 4)
-    return cls ? launch_dense<M, 4, 1>(x, ml, out_f32, K, st) : launch_dense<M, 4, 0>(x, ml, out_f32, K, st);
-  return cls ? launch_dense<M, 1, 1>(x, ml, out_f32, K, st) : launch_dense<M, 1, 0>(x, ml, out_f32, K, st);
+  return with_sched(ksplit, sched_class(nmax, K, ksplit), [&](auto ks, auto c) {
+    return launch_dense<M, decltype(ks)::value, decltype(c)::value>(x, ml, out_f32, K, st);
+  });
 }
 
 hipError_t dense_dispatch(int M, int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K,
@@ -397,20 +420,18 @@ hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* 
 template <int M>
 hipError_t lmhead_by_split(int ksplit, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                            void* logits, int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
-  const int cls = sched_class(N, K, ksplit);
-  if (ksplit == 4)
-    return cls ? launch_lmhead<M, 4, 1>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks)
-               : launch_lmhead<M, 4, 0>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks);
-  return cls ? launch_lmhead<M, 1, 1>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks)
-             : launch_lmhead<M, 1, 0>(x, qw, s, b, logits, out_f32, partial, N, K, st, nblocks);
+  return with_sched(ksplit, sched_class(N, K, ksplit), [&](auto ks, auto c) {
+    return launch_lmhead<M, decltype(ks)::value, decltype(c)::value>(x, qw, s, b, logits, out_f32, partial, N, K, st,
+                                                                     nblocks);
+  });
 }
 
 // Routed kernels: MB = most slots one expert is processed with per pass.
-template <int MB, int KSPLIT>
+template <int MB, int KSPLIT, int CLS>
 hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                          const int32_t* ids, void* y, int out_f32, int M, int top_k, int E, int N, int K,
                          hipStream_t st) {
-  using S = Sched<MB, KSPLIT, 0>;
+  using S = Sched<MB, KSPLIT, CLS>;
   using RM = RowMap<S::R, KSPLIT>;
   const int tiles = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   const size_t blocks = (size_t)tiles * M * top_k;
@@ -424,8 +445,11 @@ template <int MB>
 hipError_t routed_by_split(int ksplit, const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* s,
                            const uint16_t* b, const int32_t* ids, void* y, int out_f32, int M, int top_k, int E, int N,
                            int K, hipStream_t st) {
-  return ksplit == 4 ? launch_routed<MB, 4>(x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, st)
-                     : launch_routed<MB, 1>(x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, st);
+  // the class follows one expert's matrix (N rows), never the routed total
+  return with_sched(ksplit, sched_class(N, K, ksplit), [&](auto ks, auto c) {
+    return launch_routed<MB, decltype(ks)::value, decltype(c)::value>(x, x_per_slot, qw, s, b, ids, y, out_f32, M,
+                                                                      top_k, E, N, K, st);
+  });
 }
 
 int lmhead_blocks(int M, int N, int K) {
@@ -447,13 +471,12 @@ int lmhead_blocks(int M, int N, int K) {
 
 template <int M>
 void sched_of(int ks, int cls, int* R, int* CPL) {
-  if (ks == 4) {
-    *R = cls ? Sched<M, 4, 1>::R : Sched<M, 4, 0>::R;
-    *CPL = cls ? Sched<M, 4, 1>::CPL : Sched<M, 4, 0>::CPL;
-  } else {
-    *R = cls ? Sched<M, 1, 1>::R : Sched<M, 1, 0>::R;
-    *CPL = cls ? Sched<M, 1, 1>::CPL : Sched<M, 1, 0>::CPL;
-  }
+  with_sched(ks, cls, [&](auto k, auto c) {
+    using S = Sched<M, decltype(k)::value, decltype(c)::value>;
+    *R = S::R;
+    *CPL = S::CPL;
+    return 0;
+  });
 }
 
 }  // namespace

@@ -52,7 +52,7 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "qmm_dense_decode_step_traffic.j
 def launch_grid(kernel: str, N: int) -> int:
     """Threads launched by the dense kernel named `kernel` for N rows: blocks of
     256 threads holding 16 row groups (4 when four waves share a row) of R rows."""
-    M, R, CPL, KS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(","))
+    M, R, CPL, KS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(",")[:4])
     rows = (16 if KS == 1 else 4) * R
     return -(-N // rows) * 256
 

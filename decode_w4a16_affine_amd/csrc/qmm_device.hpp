@@ -133,7 +133,10 @@ struct Tile {
   uint32_t b[CPL][R];
 };
 
-template <int M, int R, int CS, bool FAST>
+// One 16-byte chunk (32 codes) of R rows against M activation rows.  xc points
+// at the chunk's staged activations: piece p (k = 4p .. 4p+3 of the chunk) of
+// activation row m is xc[(m * 8 + p) * PS].
+template <int M, int R, int PS, bool FAST>
 __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R], const float (&s)[R],
                                           const float (&b)[R], const float4* xc) {
   float s24[R], s20[R];
@@ -147,8 +150,8 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
     float xv[M][8];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float4 lo = xc[(m * 8 + 2 * wd) * CS];
-      const float4 hi = xc[(m * 8 + 2 * wd + 1) * CS];
+      const float4 lo = xc[(m * 8 + 2 * wd) * PS];
+      const float4 hi = xc[(m * 8 + 2 * wd + 1) * PS];
       xv[m][0] = lo.x; xv[m][1] = lo.y; xv[m][2] = lo.z; xv[m][3] = lo.w;
       xv[m][4] = hi.x; xv[m][5] = hi.y; xv[m][6] = hi.z; xv[m][7] = hi.w;
     }
@@ -186,7 +189,7 @@ struct WaveRows {
 // fold into the load instructions' immediate fields); otherwise chunk slots
 // past the end of the tile load nothing (offset outside the resource) and are
 // skipped.
-template <int M, int R, int CPL, int KSPLIT, bool FULL>
+template <int M, int R, int CPL, int KSPLIT, int PRE, bool FULL>
 __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
                                           int klen, float4* xs) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -208,24 +211,30 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
       xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + k0)[i];
     }
 
-  // 2. every weight load of the tile
+  // 2. the first PRE chunk slots of every row (the rest follow once x is staged,
+  //    so that the activation loads are not queued behind the whole tile)
   Tile<CPL, R> tl;
+  uint32_t qb[R], gb[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t lr = (uint32_t)(w.slot * R + r);
-    const uint32_t qb = lr * w.wpr * 4u + (uint32_t)(cbase + L) * 16u;   // byte offset of chunk slot 0
-    const uint32_t gb = lr * w.gpr * 2u + (uint32_t)((cbase + L) >> 1) * 2u;
+    qb[r] = lr * w.wpr * 4u + (uint32_t)(cbase + L) * 16u;   // byte offset of chunk slot 0
+    gb[r] = lr * w.gpr * 2u + (uint32_t)((cbase + L) >> 1) * 2u;
+  }
+  auto load_slot = [&](int j) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
+    for (int r = 0; r < R; ++r) {
       // chunk c = L + j*LPR; LPR is even, so its group is ((cbase + L) >> 1) + j*LPR/2
       const bool ok = FULL || L + j * LPR < cseg;
-      const uint32_t oq = ok ? qb + (uint32_t)(j * LPR * 16) : kOffNone;
-      const uint32_t og = ok ? gb + (uint32_t)(j * LPR) : kOffNone;
+      const uint32_t oq = ok ? qb[r] + (uint32_t)(j * LPR * 16) : kOffNone;
+      const uint32_t og = ok ? gb[r] + (uint32_t)(j * LPR) : kOffNone;
       tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, 0));
       tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
       tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
     }
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < (PRE < CPL ? PRE : CPL); ++j) load_slot(j);
 
   // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * CS + c]
   //    holds k = k0 + 32c + 4 piece .. +3 (CS = chunks per K-tile, a
@@ -245,6 +254,10 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
       xs[(m * 8 + piece + 1) * CS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
     }
   __syncthreads();
+
+  // the remaining weight loads of the tile
+#pragma unroll
+  for (int j = (PRE < CPL ? PRE : CPL); j < CPL; ++j) load_slot(j);
 
   // 4. consume the chunks in ascending order
 #pragma unroll
@@ -281,7 +294,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 // KSPLIT == 4: the four waves share the rows; on return every lane of every
 //              wave holds the sums (combined in wave order).
 // xs must hold M * 8 * CPL * LPR float4.  Call with all threads (barriers).
-template <int M, int R, int CPL, int KSPLIT>
+template <int M, int R, int CPL, int KSPLIT, int PRE>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -312,9 +325,9 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   for (int k0 = 0; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
     if (klen == KTILE)
-      tile_pass<M, R, CPL, KSPLIT, true>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, true>(acc, xr, w, k0, klen, xs);
     else
-      tile_pass<M, R, CPL, KSPLIT, false>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, false>(acc, xr, w, k0, klen, xs);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -339,6 +352,116 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
         acc[r][m] = v;
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming schedule (persistent waves, software-pipelined).
+//
+// The block stages the activations for the whole of K once, chunk-major:
+// chunk c occupies kXChunk<M> float4, piece p of activation row m at
+// [c * kXChunk<M> + m * 8 + p] (one float4 of padding per chunk keeps the
+// 16 lanes of a row group on distinct banks).  Each wave then walks its own
+// sequence of work items -- (row set of kSlots*R rows, K-tile of CPL chunks per
+// lane) -- with two register sets: the loads of item u+1 are in flight while
+// item u is consumed.  Lane t still owns chunks t, t+16, ... of its rows in
+// ascending order and the chunk body, reduction tree and rounding are those of
+// block_rows, so every output is bitwise the same as the block schedule's.
+// ---------------------------------------------------------------------------
+template <int M>
+constexpr int kXChunk = M * 8 + 1;
+
+struct ItemSrc {
+  __amdgpu_buffer_rsrc_t rq, rs, rb;
+};
+
+// Resources of the item (row set starting at row0, K-tile kt): they start at
+// the tile's first chunk of row0 and end with the last real row of the set, so
+// rows >= N read zero; a missing item (live == false) reads zero everywhere.
+__device__ __forceinline__ ItemSrc item_src(const RowSrc& src, int row0, int kt, int chunks_per_tile,
+                                            int rows_per_set, bool live, uint32_t wpr, uint32_t gpr) {
+  const int rows = live ? max(0, min(rows_per_set, src.N - row0)) : 0;
+  const uint32_t qskip = (uint32_t)kt * (uint32_t)chunks_per_tile * 16u;   // bytes of the row before the tile
+  const uint32_t gskip = (uint32_t)kt * (uint32_t)chunks_per_tile;         // bytes of scales before the tile
+  const uint32_t qbytes = rows > 0 ? (uint32_t)rows * wpr * 4u - qskip : 0u;
+  const uint32_t gbytes = rows > 0 ? (uint32_t)rows * gpr * 2u - gskip : 0u;
+  const size_t r0 = (size_t)(live ? row0 : 0);
+  ItemSrc is;
+  is.rq = make_rsrc(reinterpret_cast<const char*>(src.qw + r0 * wpr) + qskip, qbytes);
+  is.rs = make_rsrc(reinterpret_cast<const char*>(src.scales + r0 * gpr) + gskip, gbytes);
+  is.rb = make_rsrc(reinterpret_cast<const char*>(src.biases + r0 * gpr) + gskip, gbytes);
+  return is;
+}
+
+// Lane offsets inside an item: row slot*R + r, chunk slot j at +j*256 bytes
+// (codes) and +j*16 bytes (scales, biases: two chunks per group, 16 chunks apart).
+template <int R>
+struct LaneOff {
+  uint32_t q[R];
+  uint32_t g[R];
+};
+
+template <int CPL, int R>
+__device__ __forceinline__ void item_issue(Tile<CPL, R>& it, const ItemSrc& is, const LaneOff<R>& lo) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      it.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(is.rq, lo.q[r] + j * 256u, 0, 0));
+      it.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(is.rs, lo.g[r] + j * 16u, 0, 0);
+      it.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(is.rb, lo.g[r] + j * 16u, 0, 0);
+    }
+}
+
+// Consume one item; xw points at this lane's first chunk of the tile.
+template <int M, int R, int CPL>
+__device__ __forceinline__ void item_consume(float (&acc)[R][M], const Tile<CPL, R>& it, const float4* xw) {
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    float s[R], b[R];
+    bool plain = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      s[r] = __uint_as_float(it.s[j][r] << 16);
+      b[r] = __uint_as_float(it.b[j][r] << 16);
+      plain |= needs_plain(s[r]);
+    }
+    const float4* xc = xw + j * kRowLanes * kXChunk<M>;
+    if (__any(plain))
+      chunk_fma<M, R, 1, false>(acc, it.w[j], s, b, xc);
+    else
+      chunk_fma<M, R, 1, true>(acc, it.w[j], s, b, xc);
+  }
+}
+
+// Stage x[M, K] (bf16) into LDS as fp32 in the chunk-major layout.  XL: 16-byte
+// loads per thread and activation row, XL * kThreads * 8 >= K.  The loads are
+// issued by the caller first (x_load) so that later weight loads do not delay them.
+template <int M, int XL>
+__device__ __forceinline__ void x_load(uint4 (&xv)[M][XL], const XRows<M>& xr, int K) {
+  const int xq = K >> 3;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+      xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m])[i];
+    }
+}
+
+template <int M, int XL>
+__device__ __forceinline__ void x_store(const uint4 (&xv)[M][XL], int K, float4* xs) {
+  const int xq = K >> 3;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      // piece i covers k = 8i .. 8i+7: chunk i/4, pieces 2(i%4) and 2(i%4)+1
+      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+      const uint4 v = xv[m][j];
+      float4* d = xs + (i >> 2) * kXChunk<M> + m * 8 + 2 * (i & 3);
+      d[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+      d[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+    }
 }
 
 // Rows handled by a block and the first row of this thread's row group.

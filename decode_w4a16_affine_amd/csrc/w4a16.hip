@@ -37,6 +37,10 @@ struct Sched {
   static constexpr int R = KSPLIT == 1 ? ((CLS & 1) && M <= 5 ? 2 : 1) : 1;
   static constexpr int CPL = KSPLIT == 1 ? (M <= 3 ? ((CLS & 2) ? 5 : 4) : 3)
                                          : (M <= 3 ? (CLS == 1 && M == 1 ? 5 : 2) : 1);
+  // chunk slots whose loads go out before the activations are staged (the rest
+  // follow the staging barrier, so the activation loads are not queued behind
+  // the whole tile)
+  static constexpr int PRE = KSPLIT == 1 ? ((R == 2 || M > 1) ? 1 : (CPL == 5 ? 3 : 2)) : (CPL < 2 ? CPL : 2);
 };
 
 int sched_class(int N, int K, int ksplit) {
@@ -94,8 +98,12 @@ __device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first
     }
 }
 
-// Up to kMaxMats matrices that share K and the activations, launched together;
-// blocks [block0, next block0) of the grid stream matrix i.
+// Up to kMaxMats matrices that share K and the activations, launched together:
+// grid row blockIdx.y streams matrix blockIdx.y, and blocks past that matrix's
+// rows exit at once.  MatList is the host-side list; the kernel receives
+// MatArgs, the same fields as arrays indexed by blockIdx.y, so that every
+// field the block needs is one kernel-argument load at an offset known at
+// wave start (no chain of dependent scalar loads before the first weight load).
 constexpr int kMaxMats = 8;
 struct MatDesc {
   const uint32_t* qw;
@@ -103,26 +111,32 @@ struct MatDesc {
   const uint16_t* biases;
   void* y;
   int N;
-  int block0;
 };
 struct MatList {
   MatDesc m[kMaxMats];
   int count;
 };
+struct MatArgs {
+  const uint32_t* qw[kMaxMats];
+  const uint16_t* scales[kMaxMats];
+  const uint16_t* biases[kMaxMats];
+  void* y[kMaxMats];
+  int N[kMaxMats];
+};
 
-template <int M, int R, int CPL, int KSPLIT>
-__global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __restrict__ x, const MatList mats,
+template <int M, int R, int CPL, int KSPLIT, int PRE>
+__global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __restrict__ x, const MatArgs mats,
                                                              int out_f32, int K) {
   __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kWaves * kSlots * R * M];
   using RM = RowMap<R, KSPLIT>;
-  // this block's matrix: a uniform scan with static indices (no dynamic
-  // indexing of the argument block)
-  const int b = blockIdx.x;
-  MatDesc d = mats.m[0];
-#pragma unroll
-  for (int i = 1; i < kMaxMats; ++i)
-    if (i < mats.count && b >= mats.m[i].block0) d = mats.m[i];
+  const int mi = blockIdx.y;
+  MatDesc d{mats.qw[mi], mats.scales[mi], mats.biases[mi], mats.y[mi], mats.N[mi]};
+  // one asm that consumes every argument: all of their loads are issued before
+  // the first wait, instead of being sunk one by one to their first use
+  asm volatile("" ::"s"(d.qw), "s"(d.scales), "s"(d.biases), "s"(d.y), "s"(d.N), "s"(x), "s"(K), "s"(out_f32));
+  const int block_row0 = (int)blockIdx.x * RM::kRowsPerBlock;
+  if (block_row0 >= d.N) return;   // uniform per block: before any barrier
   XRows<M> xr;
   size_t yoff[M];
 #pragma unroll
@@ -131,13 +145,12 @@ __global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __r
     yoff[m] = (size_t)m * d.N;
   }
   const RowSrc src{d.qw, d.scales, d.biases, d.N, K};
-  const int block_row0 = (b - d.block0) * RM::kRowsPerBlock;
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT>(acc, xr, src, block_row0, xs, red);
+  block_rows<M, R, CPL, KSPLIT, PRE>(acc, xr, src, block_row0, xs, red);
   store_to<M, R, KSPLIT>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
 }
 
-template <int M, int R, int CPL, int KSPLIT>
+template <int M, int R, int CPL, int KSPLIT, int PRE>
 __global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
@@ -155,11 +168,13 @@ __global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __
     xr.p[m] = x + (size_t)m * K;
     yoff[m] = (size_t)m * N;
   }
+  asm volatile("" ::"s"(qw), "s"(scales), "s"(biases), "s"(logits), "s"(partial), "s"(x), "s"(N), "s"(K),
+               "s"(out_f32));   // every argument load issued before the first wait
   const RowSrc src{qw, scales, biases, N, K};
   const int block_row0 = blockIdx.x * RM::kRowsPerBlock;
   const int row_first = RM::first_row(block_row0);
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT>(acc, xr, src, block_row0, xs, red);
+  block_rows<M, R, CPL, KSPLIT, PRE>(acc, xr, src, block_row0, xs, red);
   if (logits) store_to<M, R, KSPLIT>(acc, row_first, N, logits, yoff, out_f32 != 0);
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -192,6 +207,94 @@ __global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __
   }
 }
 
+// Persistent streaming kernel for one matrix with KSPLIT 1 (one row group per
+// row): K is a multiple of CPL * 512, the whole of x is staged once per block,
+// and each wave walks the row sets gw, gw + GW, ... (GW = waves in the grid),
+// each in K/(CPL*512) tiles, two items in flight.
+template <int M, int R, int CPL, int XL>
+__global__ __launch_bounds__(kThreads) void qmm_stream_kernel(const uint16_t* __restrict__ x, const RowSrc src,
+                                                              void* __restrict__ y, int out_f32) {
+  extern __shared__ float4 xs[];
+  constexpr int kSet = kSlots * R;   // rows per wave item
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = lane & (kRowLanes - 1);
+  const int slot = lane / kRowLanes;
+  const int K = src.K;
+  const uint32_t wpr = (uint32_t)(K >> 3), gpr = (uint32_t)(K >> 6);
+  const int T = K / (CPL * 512);
+  const int nsets = (src.N + kSet - 1) / kSet;
+  const int GW = (int)gridDim.x * kWaves;
+  const int gw = (int)blockIdx.x * kWaves + wave;
+  const int nitems = (gw < nsets ? (nsets - 1 - gw) / GW + 1 : 0) * T;
+
+  XRows<M> xr;
+  size_t yoff[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    xr.p[m] = x + (size_t)m * K;
+    yoff[m] = (size_t)m * src.N;
+  }
+  uint4 xv[M][XL];
+  x_load<M, XL>(xv, xr, K);
+
+  LaneOff<R> lo;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t lr = (uint32_t)(slot * R + r);
+    lo.q[r] = lr * wpr * 4u + (uint32_t)t * 16u;
+    lo.g[r] = lr * gpr * 2u + (uint32_t)(t >> 1) * 2u;
+  }
+
+  int iss_set = gw, iss_kt = 0, issued = 0;   // next item to issue
+  auto next_src = [&]() {
+    const ItemSrc is = item_src(src, iss_set * kSet, iss_kt, CPL * kRowLanes, kSet, issued < nitems, wpr, gpr);
+    ++issued;
+    if (++iss_kt == T) {
+      iss_kt = 0;
+      iss_set += GW;
+    }
+    return is;
+  };
+  Tile<CPL, R> A, B;
+  item_issue<CPL, R>(A, next_src(), lo);
+  item_issue<CPL, R>(B, next_src(), lo);
+  x_store<M, XL>(xv, K, xs);
+  __syncthreads();
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  int c_set = gw, c_kt = 0;   // item being consumed
+  const float4* xlane = xs + t * kXChunk<M>;
+  auto finish = [&]() {
+    if (++c_kt == T) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = row16_sum(acc[r][m]);
+      store_to<M, R, 1>(acc, c_set * kSet + slot * R, src.N, y, yoff, out_f32 != 0);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+      c_kt = 0;
+      c_set += GW;
+    }
+  };
+  for (int u = 0; u < nitems; u += 2) {
+    item_consume<M, R, CPL>(acc, A, xlane + c_kt * CPL * kRowLanes * kXChunk<M>);
+    finish();
+    item_issue<CPL, R>(A, next_src(), lo);
+    if (u + 1 >= nitems) break;
+    item_consume<M, R, CPL>(acc, B, xlane + c_kt * CPL * kRowLanes * kXChunk<M>);
+    finish();
+    item_issue<CPL, R>(B, next_src(), lo);
+  }
+}
+
 __global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __restrict__ partial, int nblocks, int M,
                                                               int32_t* __restrict__ argmax) {
   __shared__ uint64_t s[256];
@@ -211,7 +314,7 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __
 }
 
 // One pass of the routed product: C slots routed to one expert.
-template <int C, int R, int CPL, int KSPLIT>
+template <int C, int R, int CPL, int KSPLIT, int PRE>
 __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, int x_per_slot, int top_k,
                                             const RowSrc& src, int block_row0, void* y, bool out_f32, float4* xs,
                                             float* red) {
@@ -225,11 +328,11 @@ __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, 
     yoff[i] = (size_t)sl * src.N;
   }
   float acc[R][C];
-  block_rows<C, R, CPL, KSPLIT>(acc, xr, src, block_row0, xs, red);
+  block_rows<C, R, CPL, KSPLIT, PRE>(acc, xr, src, block_row0, xs, red);
   store_to<C, R, KSPLIT>(acc, RM::first_row(block_row0), src.N, y, yoff, out_f32);
 }
 
-template <int MB, int R, int CPL, int KSPLIT>
+template <int MB, int R, int CPL, int KSPLIT, int PRE>
 __global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __restrict__ x, int x_per_slot,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
@@ -271,14 +374,14 @@ __global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __
       if (ids[j] == e) list[cnt++] = j;
     if (cnt == 0) break;
     switch (cnt) {
-      case 1: routed_pass<1, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 4: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 5: if constexpr (MB >= 5) routed_pass<5, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 6: if constexpr (MB >= 6) routed_pass<6, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 7: if constexpr (MB >= 7) routed_pass<7, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      default: if constexpr (MB >= 8) routed_pass<8, R, CPL, KSPLIT>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 1: routed_pass<1, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 4: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 5: if constexpr (MB >= 5) routed_pass<5, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 6: if constexpr (MB >= 6) routed_pass<6, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 7: if constexpr (MB >= 7) routed_pass<7, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      default: if constexpr (MB >= 8) routed_pass<8, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
     }
   }
 }
@@ -351,33 +454,60 @@ w4a16_status_t check_weights(const uint16_t* x, const uint32_t* qw, const uint16
   return W4A16_OK;
 }
 
-template <int M, int R, int CPL, int KSPLIT>
-hipError_t launch_dense_list(const uint16_t* x, MatList ml, int out_f32, int K, hipStream_t st) {
+template <int M, int R, int CPL, int KSPLIT, int PRE>
+hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   using RM = RowMap<R, KSPLIT>;
   long blocks = 0;
+  MatArgs a{};
   for (int i = 0; i < ml.count; ++i) {
-    ml.m[i].block0 = (int)blocks;
-    blocks += (ml.m[i].N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
+    const long bi = (ml.m[i].N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
+    blocks = bi > blocks ? bi : blocks;
+    a.qw[i] = ml.m[i].qw;
+    a.scales[i] = ml.m[i].scales;
+    a.biases[i] = ml.m[i].biases;
+    a.y[i] = ml.m[i].y;
+    a.N[i] = ml.m[i].N;
   }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT>), dim3((unsigned)blocks), dim3(kThreads), 0, st, x, ml,
-                     out_f32, K);
+  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE>), dim3((unsigned)blocks, (unsigned)ml.count),
+                     dim3(kThreads), 0, st, x, a, out_f32, K);
   return hipGetLastError();
 }
 
-template <int M, int R, int CPL, int KSPLIT>
+template <int M, int R, int CPL, int KSPLIT, int PRE = CPL>
 hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
                               int out_f32, int N, int K, hipStream_t st) {
   MatList ml{};
-  ml.m[0] = MatDesc{qw, s, b, y, N, 0};
+  ml.m[0] = MatDesc{qw, s, b, y, N};
   ml.count = 1;
-  return launch_dense_list<M, R, CPL, KSPLIT>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, R, CPL, KSPLIT, PRE>(x, ml, out_f32, K, st);
+}
+
+template <int M>
+size_t stream_lds_bytes(int K) { return (size_t)(K / 32) * kXChunk<M> * sizeof(float4); }
+
+template <int M, int R, int CPL, int XL>
+hipError_t launch_stream(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
+                         int out_f32, int N, int K, int grid, hipStream_t st) {
+  const size_t lds = stream_lds_bytes<M>(K);
+  if (lds > 65536) {
+    static bool raised = false;   // the attribute is per function; setting it twice is harmless
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_stream_kernel<M, R, CPL, XL>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  const RowSrc src{qw, s, b, N, K};
+  hipLaunchKernelGGL((qmm_stream_kernel<M, R, CPL, XL>), dim3(grid), dim3(kThreads), lds, st, x, src, y, out_f32);
+  return hipGetLastError();
 }
 
 template <int M, int KSPLIT, int CLS>
 hipError_t launch_dense(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   using S = Sched<M, KSPLIT, CLS>;
-  return launch_dense_list<M, S::R, S::CPL, KSPLIT>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE>(x, ml, out_f32, K, st);
 }
 
 // Every matrix of `ml` must have the K-split `ksplit`; the schedule class
@@ -412,7 +542,7 @@ hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* 
   using RM = RowMap<S::R, KSPLIT>;
   const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   *nblocks = blocks;
-  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT>), dim3(blocks), dim3(kThreads), 0, st, x, qw, s, b,
+  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT, S::PRE>), dim3(blocks), dim3(kThreads), 0, st, x, qw, s, b,
                      logits, out_f32, partial, N, K);
   return hipGetLastError();
 }
@@ -436,7 +566,7 @@ hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, 
   const int tiles = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   const size_t blocks = (size_t)tiles * M * top_k;
   if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
                      x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, tiles);
   return hipGetLastError();
 }
@@ -470,9 +600,10 @@ int lmhead_blocks(int M, int N, int K) {
 }
 
 template <int M>
-void sched_of(int ks, int cls, int* R, int* CPL) {
+void sched_of(int ks, int cls, int* R, int* CPL, int* PRE) {
   with_sched(ks, cls, [&](auto k, auto c) {
     using S = Sched<M, decltype(k)::value, decltype(c)::value>;
+    *PRE = S::PRE;
     *R = S::R;
     *CPL = S::CPL;
     return 0;
@@ -489,18 +620,18 @@ const char* w4a16_schedule_name(int M, int N, int K, int group) {
   static thread_local char buf[96];
   if (check_shape(M, N, K, group, W4A16_OUT_BF16) != W4A16_OK || M == 0 || N == 0) return "";
   const int ks = ksplit_for(N, K), cls = sched_class(N, K, ks);
-  int R = 0, CPL = 0;
+  int R = 0, CPL = 0, PRE = 0;
   switch (M) {
-    case 1: sched_of<1>(ks, cls, &R, &CPL); break;
-    case 2: sched_of<2>(ks, cls, &R, &CPL); break;
-    case 3: sched_of<3>(ks, cls, &R, &CPL); break;
-    case 4: sched_of<4>(ks, cls, &R, &CPL); break;
-    case 5: sched_of<5>(ks, cls, &R, &CPL); break;
-    case 6: sched_of<6>(ks, cls, &R, &CPL); break;
-    case 7: sched_of<7>(ks, cls, &R, &CPL); break;
-    default: sched_of<8>(ks, cls, &R, &CPL); break;
+    case 1: sched_of<1>(ks, cls, &R, &CPL, &PRE); break;
+    case 2: sched_of<2>(ks, cls, &R, &CPL, &PRE); break;
+    case 3: sched_of<3>(ks, cls, &R, &CPL, &PRE); break;
+    case 4: sched_of<4>(ks, cls, &R, &CPL, &PRE); break;
+    case 5: sched_of<5>(ks, cls, &R, &CPL, &PRE); break;
+    case 6: sched_of<6>(ks, cls, &R, &CPL, &PRE); break;
+    case 7: sched_of<7>(ks, cls, &R, &CPL, &PRE); break;
+    default: sched_of<8>(ks, cls, &R, &CPL, &PRE); break;
   }
-  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d>", M, R, CPL, ks);
+  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d, %d>", M, R, CPL, ks, PRE);
   return buf;
 }
 
@@ -525,7 +656,7 @@ w4a16_status_t w4a16_matmul(const uint16_t* x, const uint32_t* qw, const uint16_
   st = check_weights(x, qw, scales, biases, y, out_dtype);
   if (st != W4A16_OK) return st;
   MatList ml{};
-  ml.m[0] = MatDesc{qw, scales, biases, y, N, 0};
+  ml.m[0] = MatDesc{qw, scales, biases, y, N};
   ml.count = 1;
   return launched(dense_dispatch(M, ksplit_for(N, K), x, ml, out_dtype == W4A16_OUT_F32, K, (hipStream_t)stream));
 }
@@ -554,7 +685,7 @@ w4a16_status_t w4a16_matmul_grouped(const uint16_t* x, const w4a16_matrix_t* mat
     ml.count = 0;
     for (int i = 0; i < count; ++i)
       if (mats[i].N > 0 && ksplit_for(mats[i].N, K) == ks)
-        ml.m[ml.count++] = MatDesc{mats[i].qw, mats[i].scales, mats[i].biases, mats[i].y, mats[i].N, 0};
+        ml.m[ml.count++] = MatDesc{mats[i].qw, mats[i].scales, mats[i].biases, mats[i].y, mats[i].N};
     if (ml.count == 0) continue;
     const hipError_t e = dense_dispatch(M, ks, x, ml, out_dtype == W4A16_OUT_F32, K, (hipStream_t)stream);
     if (e != hipSuccess) return W4A16_ERR_HIP;

@@ -49,12 +49,15 @@ def step_bytes(M: int, layers: int) -> int:
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "qmm_dense_decode_step_traffic.json")
 
 
-def launch_grid(kernel: str, N: int) -> int:
-    """Threads launched by the dense kernel named `kernel` for N rows: blocks of
-    256 threads holding 16 row groups (4 when four waves share a row) of R rows."""
+def launch_grid(kernel: str, Ns) -> int:
+    """Work-items launched by the dense kernel named `kernel` for matrices of
+    Ns rows sharing one launch: a grid of (blocks of the tallest matrix) x
+    (matrices) blocks; a block is 4 waves holding 16 row groups of R rows, or,
+    with a K-split of S, S waves sharing 4 row groups of R rows."""
     M, R, CPL, KS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(",")[:4])
     rows = (16 if KS == 1 else 4) * R
-    return -(-N // rows) * 256
+    threads = 64 * (4 if KS == 1 else KS)
+    return -(-max(Ns) // rows) * len(Ns) * threads
 
 
 def log(*a):
@@ -242,7 +245,7 @@ def main():
         e["bytes_total"] += unit_bytes(1, ps)
         e["launches"] += 1
         e["units"].append(u)
-        e["grids"].append(sum(launch_grid(kern, synthetic.PROJECTIONS[p][0]) for p in ps))
+        e["grids"].append(launch_grid(kern, [synthetic.PROJECTIONS[p][0] for p in ps]))
     dom = max(per_group, key=lambda k: per_group[k]["us_total"])
     pg = per_group[dom]
     avg_us = pg["us_total"] / pg["launches"]

@@ -29,10 +29,17 @@
 namespace w4k {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                      // waves per block without K-split
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowLanes = 16;
 constexpr int kSlots = kWave / kRowLanes;      // row groups per wave
+
+// Block shape for a K-split of S (KSPLIT): without a split, four waves hold
+// 16 rows; with one, each of S waves holds one S-th of the same four rows.
+template <int KSPLIT>
+constexpr int kBlockWaves = KSPLIT == 1 ? kWaves : KSPLIT;
+template <int KSPLIT>
+constexpr int kBlockThreads = kWave * kBlockWaves<KSPLIT>;
 constexpr int kMaxM = 8;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -195,7 +202,8 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
   constexpr int LPR = kRowLanes * KSPLIT;
   constexpr int CS = CPL * LPR;                               // chunks per K-tile
   constexpr int KTILE = CS * 32;                              // codes per K-tile
-  constexpr int XL = (KTILE / 8 + kThreads - 1) / kThreads;   // 16-byte x loads per thread per row
+  constexpr int NT = kBlockThreads<KSPLIT>;
+  constexpr int XL = (KTILE / 8 + NT - 1) / NT;                // 16-byte x loads per thread per row
   const int cseg = FULL ? CS : klen >> 5;    // chunks in this tile
   const int cbase = k0 >> 5;
   const int xq = FULL ? KTILE / 8 : klen >> 3;  // 16-byte x pieces per row in this tile
@@ -207,7 +215,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
-      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+      const int i = min((int)threadIdx.x + j * NT, xq - 1);
       xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + k0)[i];
     }
 
@@ -246,7 +254,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
-      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
+      const int i = min((int)threadIdx.x + j * NT, xq - 1);
       const int kk = 8 * i;
       const int c = kk >> 5, piece = (kk >> 2) & 7;
       const uint4 v = xv[m][j];
@@ -282,7 +290,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 
 // Full-row sums for the R rows of this lane's row group.
 //
-// Lane L of a row (L = t for KSPLIT 1, wave*16 + t for KSPLIT 4) owns the
+// Lane L of a row (L = t without K-split, wave*16 + t with one) owns the
 // 16-byte chunks c = L, L + LPR, L + 2 LPR, ... of the row and accumulates
 // them in ascending order; the row is walked in K-tiles of CPL * LPR chunks.
 // Per K-tile: the activation loads are issued first, then every weight load
@@ -291,8 +299,8 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 // chunks are consumed in order as they arrive.
 //
 // KSPLIT == 1: on return every lane of the row group holds the sums.
-// KSPLIT == 4: the four waves share the rows; on return every lane of every
-//              wave holds the sums (combined in wave order).
+// KSPLIT == S > 1: the S waves of the block share the rows; on return every
+//              lane of every wave holds the sums (combined in wave order).
 // xs must hold M * 8 * CPL * LPR float4.  Call with all threads (barriers).
 template <int M, int R, int CPL, int KSPLIT, int PRE>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,

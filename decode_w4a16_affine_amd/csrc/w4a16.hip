@@ -23,7 +23,13 @@ namespace {
 
 constexpr int kNarrowN = 4096;
 
-int ksplit_for(int N, int /*K*/) { return N <= kNarrowN ? 4 : 1; }
+// K-split: narrow matrices spread each row over several waves so that the
+// grid fills the chip and no lane holds more than a few chunks.  A split of 5
+// gives rows of K = 2560 (80 chunks) exactly one chunk per lane.
+int ksplit_for(int N, int K) {
+  if (N > kNarrowN) return 1;
+  return (K % 2560 == 0 && K <= 5120) ? 5 : 4;
+}
 
 // Schedules measured on MI355X (cold weights, graph-replayed launches).
 //
@@ -32,18 +38,32 @@ int ksplit_for(int N, int /*K*/) { return N <= kNarrowN ? 4 : 1; }
 // tiles of 5 chunks per lane cover K exactly, otherwise 4): tiles that cover K
 // exactly use straight-line loads with immediate offsets.
 // KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile.
+// PRE: chunk slots whose loads go out before the activations are staged (the
+// rest follow the staging barrier, so the activation loads are not queued
+// behind the whole tile).
 template <int M, int KSPLIT, int CLS>
-struct Sched {
-  static constexpr int R = KSPLIT == 1 ? ((CLS & 1) && M <= 5 ? 2 : 1) : 1;
-  static constexpr int CPL = KSPLIT == 1 ? (M <= 3 ? ((CLS & 2) ? 5 : 4) : 3)
-                                         : (M <= 3 ? (CLS == 1 && M == 1 ? 5 : 2) : 1);
-  // chunk slots whose loads go out before the activations are staged (the rest
-  // follow the staging barrier, so the activation loads are not queued behind
-  // the whole tile)
-  static constexpr int PRE = KSPLIT == 1 ? ((R == 2 || M > 1) ? 1 : (CPL == 5 ? 3 : 2)) : (CPL < 2 ? CPL : 2);
+struct Sched;
+template <int M, int CLS>
+struct Sched<M, 1, CLS> {
+  static constexpr int R = (CLS & 1) && M <= 5 ? 2 : 1;
+  static constexpr int CPL = M <= 3 ? ((CLS & 2) ? 5 : 4) : (((CLS & 2) && R == 1) ? 5 : 3);
+  static constexpr int PRE = (R == 2 || M > 1) ? 1 : (CPL == 5 ? 3 : 2);
+};
+template <int M, int CLS>
+struct Sched<M, 4, CLS> {
+  static constexpr int R = (CLS == 1 && M >= 3) ? 2 : 1;
+  static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 && R == 1 ? 2 : 1);
+  static constexpr int PRE = CPL < 2 ? CPL : 2;
+};
+template <int M, int CLS>
+struct Sched<M, 5, CLS> {
+  static constexpr int R = M == 1 ? 1 : 2;
+  static constexpr int CPL = 1;
+  static constexpr int PRE = 1;
 };
 
 int sched_class(int N, int K, int ksplit) {
+  if (ksplit == 5) return 0;
   if (ksplit == 4) return K > 4096;
   return (N >= 131072 ? 1 : 0) | (K % 2048 != 0 && K % 2560 == 0 ? 2 : 0);
 }
@@ -52,6 +72,7 @@ int sched_class(int N, int K, int ksplit) {
 template <typename F>
 auto with_sched(int ksplit, int cls, F&& f) {
   using std::integral_constant;
+  if (ksplit == 5) return f(integral_constant<int, 5>{}, integral_constant<int, 0>{});
   if (ksplit == 4)
     return cls ? f(integral_constant<int, 4>{}, integral_constant<int, 1>{})
                : f(integral_constant<int, 4>{}, integral_constant<int, 0>{});
@@ -105,6 +126,7 @@ __device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first
 // field the block needs is one kernel-argument load at an offset known at
 // wave start (no chain of dependent scalar loads before the first weight load).
 constexpr int kMaxMats = 8;
+static_assert(kMaxMats >= W4A16_MAX_GROUP, "a grouped launch must hold every matrix of a call");
 struct MatDesc {
   const uint32_t* qw;
   const uint16_t* scales;
@@ -125,10 +147,10 @@ struct MatArgs {
 };
 
 template <int M, int R, int CPL, int KSPLIT, int PRE>
-__global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __restrict__ x, const MatArgs mats,
-                                                             int out_f32, int K) {
+__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(const uint16_t* __restrict__ x,
+                                                                          const MatArgs mats, int out_f32, int K) {
   __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
-  __shared__ float red[kWaves * kSlots * R * M];
+  __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
   using RM = RowMap<R, KSPLIT>;
   const int mi = blockIdx.y;
   MatDesc d{mats.qw[mi], mats.scales[mi], mats.biases[mi], mats.y[mi], mats.N[mi]};
@@ -151,15 +173,15 @@ __global__ __launch_bounds__(kThreads) void qmm_dense_kernel(const uint16_t* __r
 }
 
 template <int M, int R, int CPL, int KSPLIT, int PRE>
-__global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const uint16_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint16_t* __restrict__ biases,
                                                               void* __restrict__ logits, int out_f32,
                                                               uint64_t* __restrict__ partial, int N, int K) {
   __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
-  __shared__ float red[kWaves * kSlots * R * M];
-  __shared__ uint64_t keys[kWaves * kSlots][M];
+  __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
+  __shared__ uint64_t keys[kBlockWaves<KSPLIT> * kSlots][M];
   using RM = RowMap<R, KSPLIT>;
   XRows<M> xr;
   size_t yoff[M];
@@ -199,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void qmm_lmhead_kernel(const uint16_t* __
   __syncthreads();
   if (threadIdx.x < M) {
     uint64_t best = 0;
-    for (int i = 0; i < kWaves * kSlots; ++i) {
+    for (int i = 0; i < kBlockWaves<KSPLIT> * kSlots; ++i) {
       const uint64_t k = keys[i][threadIdx.x];
       best = k > best ? k : best;
     }
@@ -333,7 +355,7 @@ __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, 
 }
 
 template <int MB, int R, int CPL, int KSPLIT, int PRE>
-__global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __restrict__ x, int x_per_slot,
+__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(const uint16_t* __restrict__ x, int x_per_slot,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint16_t* __restrict__ biases,
@@ -341,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __
                                                               int out_f32, int M, int top_k, int E, int N, int K,
                                                               int tiles) {
   __shared__ float4 xs[MB * 8 * CPL * kRowLanes * KSPLIT];
-  __shared__ float red[kWaves * kSlots * R * MB];
+  __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * MB];
   using RM = RowMap<R, KSPLIT>;
   const int nslots = M * top_k;
   const int slot = blockIdx.x / tiles;
@@ -350,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void qmm_routed_kernel(const uint16_t* __
   const int e = ids[slot];
   if (e < 0 || e >= E) {
     // precondition violation: make the slot's output unmistakable
-    for (int i = threadIdx.x; i < RM::kRowsPerBlock; i += kThreads) {
+    for (int i = threadIdx.x; i < RM::kRowsPerBlock; i += kBlockThreads<KSPLIT>) {
       const int n = block_row0 + i;
       if (n < N) {
         if (out_f32)
@@ -470,7 +492,7 @@ hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, 
   }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE>), dim3((unsigned)blocks, (unsigned)ml.count),
-                     dim3(kThreads), 0, st, x, a, out_f32, K);
+                     dim3(kBlockThreads<KSPLIT>), 0, st, x, a, out_f32, K);
   return hipGetLastError();
 }
 
@@ -542,7 +564,8 @@ hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* 
   using RM = RowMap<S::R, KSPLIT>;
   const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   *nblocks = blocks;
-  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT, S::PRE>), dim3(blocks), dim3(kThreads), 0, st, x, qw, s, b,
+  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT, S::PRE>), dim3(blocks), dim3(kBlockThreads<KSPLIT>), 0,
+                     st, x, qw, s, b,
                      logits, out_f32, partial, N, K);
   return hipGetLastError();
 }
@@ -566,7 +589,8 @@ hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, 
   const int tiles = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   const size_t blocks = (size_t)tiles * M * top_k;
   if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE>), dim3((unsigned)blocks),
+                     dim3(kBlockThreads<KSPLIT>), 0, st,
                      x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, tiles);
   return hipGetLastError();
 }
@@ -679,14 +703,19 @@ w4a16_status_t w4a16_matmul_grouped(const uint16_t* x, const w4a16_matrix_t* mat
     w4a16_status_t st = check_weights(x, mats[i].qw, mats[i].scales, mats[i].biases, mats[i].y, out_dtype);
     if (st != W4A16_OK) return st;
   }
-  // one launch per K-split class (all matrices of a decode layer's q/k/v share one)
-  for (int ks : {4, 1}) {
+  // one launch per distinct K-split among the matrices (the q/k/v of a decode
+  // layer share one), in order of first appearance
+  bool done[W4A16_MAX_GROUP] = {};
+  for (int first = 0; first < count; ++first) {
+    if (done[first] || mats[first].N == 0) continue;
+    const int ks = ksplit_for(mats[first].N, K);
     MatList ml{};
     ml.count = 0;
-    for (int i = 0; i < count; ++i)
-      if (mats[i].N > 0 && ksplit_for(mats[i].N, K) == ks)
+    for (int i = first; i < count; ++i)
+      if (!done[i] && mats[i].N > 0 && ksplit_for(mats[i].N, K) == ks) {
         ml.m[ml.count++] = MatDesc{mats[i].qw, mats[i].scales, mats[i].biases, mats[i].y, mats[i].N};
-    if (ml.count == 0) continue;
+        done[i] = true;
+      }
     const hipError_t e = dense_dispatch(M, ks, x, ml, out_dtype == W4A16_OUT_F32, K, (hipStream_t)stream);
     if (e != hipSuccess) return W4A16_ERR_HIP;
   }

@@ -130,7 +130,7 @@ def test_decode_projections_and_verify_batches(orc, name):
             assert np.array_equal(yb[m], singlesb[m]), (name, M, m)
 
 
-RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560)]
+RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560), (61, 2560), (300, 5120)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)

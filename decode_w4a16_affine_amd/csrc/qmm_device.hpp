@@ -196,7 +196,7 @@ struct WaveRows {
 // fold into the load instructions' immediate fields); otherwise chunk slots
 // past the end of the tile load nothing (offset outside the resource) and are
 // skipped.
-template <int M, int R, int CPL, int KSPLIT, int PRE, bool FULL>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL>
 __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
                                           int klen, float4* xs) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -241,8 +241,13 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
       tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
     }
   };
+  // DEPTH: chunk slots in flight per lane; the load of slot j + DEPTH goes out
+  // when slot j is consumed, so the arrivals of every wave spread over the tile
+  // instead of all landing together (DEPTH >= CPL: every load up front).
+  constexpr int D = DEPTH < CPL ? DEPTH : CPL;
+  constexpr int P0 = PRE < D ? PRE : D;
 #pragma unroll
-  for (int j = 0; j < (PRE < CPL ? PRE : CPL); ++j) load_slot(j);
+  for (int j = 0; j < P0; ++j) load_slot(j);
 
   // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * CS + c]
   //    holds k = k0 + 32c + 4 piece .. +3 (CS = chunks per K-tile, a
@@ -263,13 +268,14 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
     }
   __syncthreads();
 
-  // the remaining weight loads of the tile
+  // the rest of the first DEPTH slots
 #pragma unroll
-  for (int j = (PRE < CPL ? PRE : CPL); j < CPL; ++j) load_slot(j);
+  for (int j = P0; j < D; ++j) load_slot(j);
 
   // 4. consume the chunks in ascending order
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
+    if (j + D < CPL) load_slot(j + D);
     const int c = L + j * LPR;
     if (FULL || c < cseg) {
       float s[R], b[R];
@@ -302,7 +308,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 // KSPLIT == S > 1: the S waves of the block share the rows; on return every
 //              lane of every wave holds the sums (combined in wave order).
 // xs must hold M * 8 * CPL * LPR float4.  Call with all threads (barriers).
-template <int M, int R, int CPL, int KSPLIT, int PRE>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -333,9 +339,9 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   for (int k0 = 0; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
     if (klen == KTILE)
-      tile_pass<M, R, CPL, KSPLIT, PRE, true>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true>(acc, xr, w, k0, klen, xs);
     else
-      tile_pass<M, R, CPL, KSPLIT, PRE, false>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false>(acc, xr, w, k0, klen, xs);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)

@@ -40,26 +40,31 @@ int ksplit_for(int N, int K) {
 // KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile.
 // PRE: chunk slots whose loads go out before the activations are staged (the
 // rest follow the staging barrier, so the activation loads are not queued
-// behind the whole tile).
+// behind the whole tile).  DEPTH: chunk slots in flight per lane; later slots
+// are issued as earlier ones are consumed, which spreads every wave's arrivals
+// over the launch instead of leaving whole waves of work for the end.
 template <int M, int KSPLIT, int CLS>
 struct Sched;
 template <int M, int CLS>
 struct Sched<M, 1, CLS> {
   static constexpr int R = (CLS & 1) && M <= 5 ? 2 : 1;
   static constexpr int CPL = M <= 3 ? ((CLS & 2) ? 5 : 4) : (((CLS & 2) && R == 1) ? 5 : 3);
-  static constexpr int PRE = (R == 2 || M > 1) ? 1 : (CPL == 5 ? 3 : 2);
+  static constexpr int PRE = 1;
+  static constexpr int DEPTH = (R == 2 && M == 1) ? 3 : 2;
 };
 template <int M, int CLS>
 struct Sched<M, 4, CLS> {
   static constexpr int R = (CLS == 1 && M >= 3) ? 2 : 1;
   static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 && R == 1 ? 2 : 1);
-  static constexpr int PRE = CPL < 2 ? CPL : 2;
+  static constexpr int PRE = 1;
+  static constexpr int DEPTH = 2;
 };
 template <int M, int CLS>
 struct Sched<M, 5, CLS> {
   static constexpr int R = M == 1 ? 1 : 2;
   static constexpr int CPL = 1;
   static constexpr int PRE = 1;
+  static constexpr int DEPTH = 1;
 };
 
 int sched_class(int N, int K, int ksplit) {
@@ -146,7 +151,7 @@ struct MatArgs {
   int N[kMaxMats];
 };
 
-template <int M, int R, int CPL, int KSPLIT, int PRE>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(const uint16_t* __restrict__ x,
                                                                           const MatArgs mats, int out_f32, int K) {
   __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
@@ -168,11 +173,11 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(const 
   }
   const RowSrc src{d.qw, d.scales, d.biases, d.N, K};
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT, PRE>(acc, xr, src, block_row0, xs, red);
+  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH>(acc, xr, src, block_row0, xs, red);
   store_to<M, R, KSPLIT>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const uint16_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
   const int block_row0 = blockIdx.x * RM::kRowsPerBlock;
   const int row_first = RM::first_row(block_row0);
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT, PRE>(acc, xr, src, block_row0, xs, red);
+  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH>(acc, xr, src, block_row0, xs, red);
   if (logits) store_to<M, R, KSPLIT>(acc, row_first, N, logits, yoff, out_f32 != 0);
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __
 }
 
 // One pass of the routed product: C slots routed to one expert.
-template <int C, int R, int CPL, int KSPLIT, int PRE>
+template <int C, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, int x_per_slot, int top_k,
                                             const RowSrc& src, int block_row0, void* y, bool out_f32, float4* xs,
                                             float* red) {
@@ -350,11 +355,11 @@ __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, 
     yoff[i] = (size_t)sl * src.N;
   }
   float acc[R][C];
-  block_rows<C, R, CPL, KSPLIT, PRE>(acc, xr, src, block_row0, xs, red);
+  block_rows<C, R, CPL, KSPLIT, PRE, DEPTH>(acc, xr, src, block_row0, xs, red);
   store_to<C, R, KSPLIT>(acc, RM::first_row(block_row0), src.N, y, yoff, out_f32);
 }
 
-template <int MB, int R, int CPL, int KSPLIT, int PRE>
+template <int MB, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(const uint16_t* __restrict__ x, int x_per_slot,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
@@ -396,14 +401,14 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(const
       if (ids[j] == e) list[cnt++] = j;
     if (cnt == 0) break;
     switch (cnt) {
-      case 1: routed_pass<1, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 4: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 5: if constexpr (MB >= 5) routed_pass<5, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 6: if constexpr (MB >= 6) routed_pass<6, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 7: if constexpr (MB >= 7) routed_pass<7, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      default: if constexpr (MB >= 8) routed_pass<8, R, CPL, KSPLIT, PRE>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 1: routed_pass<1, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 4: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 5: if constexpr (MB >= 5) routed_pass<5, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 6: if constexpr (MB >= 6) routed_pass<6, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      case 7: if constexpr (MB >= 7) routed_pass<7, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      default: if constexpr (MB >= 8) routed_pass<8, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
     }
   }
 }
@@ -476,7 +481,7 @@ w4a16_status_t check_weights(const uint16_t* x, const uint32_t* qw, const uint16
   return W4A16_OK;
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   using RM = RowMap<R, KSPLIT>;
   long blocks = 0;
@@ -491,18 +496,18 @@ hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, 
     a.N[i] = ml.m[i].N;
   }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE>), dim3((unsigned)blocks, (unsigned)ml.count),
+  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH>), dim3((unsigned)blocks, (unsigned)ml.count),
                      dim3(kBlockThreads<KSPLIT>), 0, st, x, a, out_f32, K);
   return hipGetLastError();
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE = CPL>
+template <int M, int R, int CPL, int KSPLIT, int PRE = CPL, int DEPTH = CPL>
 hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
                               int out_f32, int N, int K, hipStream_t st) {
   MatList ml{};
   ml.m[0] = MatDesc{qw, s, b, y, N};
   ml.count = 1;
-  return launch_dense_list<M, R, CPL, KSPLIT, PRE>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, R, CPL, KSPLIT, PRE, DEPTH>(x, ml, out_f32, K, st);
 }
 
 template <int M>
@@ -529,7 +534,7 @@ hipError_t launch_stream(const uint16_t* x, const uint32_t* qw, const uint16_t* 
 template <int M, int KSPLIT, int CLS>
 hipError_t launch_dense(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   using S = Sched<M, KSPLIT, CLS>;
-  return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH>(x, ml, out_f32, K, st);
 }
 
 // Every matrix of `ml` must have the K-split `ksplit`; the schedule class
@@ -564,7 +569,7 @@ hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* 
   using RM = RowMap<S::R, KSPLIT>;
   const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   *nblocks = blocks;
-  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT, S::PRE>), dim3(blocks), dim3(kBlockThreads<KSPLIT>), 0,
+  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH>), dim3(blocks), dim3(kBlockThreads<KSPLIT>), 0,
                      st, x, qw, s, b,
                      logits, out_f32, partial, N, K);
   return hipGetLastError();
@@ -589,7 +594,7 @@ hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, 
   const int tiles = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   const size_t blocks = (size_t)tiles * M * top_k;
   if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH>), dim3((unsigned)blocks),
                      dim3(kBlockThreads<KSPLIT>), 0, st,
                      x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, tiles);
   return hipGetLastError();
@@ -624,10 +629,11 @@ int lmhead_blocks(int M, int N, int K) {
 }
 
 template <int M>
-void sched_of(int ks, int cls, int* R, int* CPL, int* PRE) {
+void sched_of(int ks, int cls, int* R, int* CPL, int* PRE, int* DEPTH) {
   with_sched(ks, cls, [&](auto k, auto c) {
     using S = Sched<M, decltype(k)::value, decltype(c)::value>;
     *PRE = S::PRE;
+    *DEPTH = S::DEPTH;
     *R = S::R;
     *CPL = S::CPL;
     return 0;
@@ -644,18 +650,18 @@ const char* w4a16_schedule_name(int M, int N, int K, int group) {
   static thread_local char buf[96];
   if (check_shape(M, N, K, group, W4A16_OUT_BF16) != W4A16_OK || M == 0 || N == 0) return "";
   const int ks = ksplit_for(N, K), cls = sched_class(N, K, ks);
-  int R = 0, CPL = 0, PRE = 0;
+  int R = 0, CPL = 0, PRE = 0, DEPTH = 0;
   switch (M) {
-    case 1: sched_of<1>(ks, cls, &R, &CPL, &PRE); break;
-    case 2: sched_of<2>(ks, cls, &R, &CPL, &PRE); break;
-    case 3: sched_of<3>(ks, cls, &R, &CPL, &PRE); break;
-    case 4: sched_of<4>(ks, cls, &R, &CPL, &PRE); break;
-    case 5: sched_of<5>(ks, cls, &R, &CPL, &PRE); break;
-    case 6: sched_of<6>(ks, cls, &R, &CPL, &PRE); break;
-    case 7: sched_of<7>(ks, cls, &R, &CPL, &PRE); break;
-    default: sched_of<8>(ks, cls, &R, &CPL, &PRE); break;
+    case 1: sched_of<1>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    case 2: sched_of<2>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    case 3: sched_of<3>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    case 4: sched_of<4>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    case 5: sched_of<5>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    case 6: sched_of<6>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    case 7: sched_of<7>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    default: sched_of<8>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
   }
-  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d, %d>", M, R, CPL, ks, PRE);
+  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d, %d, %d>", M, R, CPL, ks, PRE, DEPTH);
   return buf;
 }
 

@@ -174,9 +174,10 @@ const char *w4a16_status_str(w4a16_status_t s);
 
 /*
  * Name of the kernel instantiation w4a16_matmul launches for this shape, as
- * profilers report it ("qmm_dense_kernel<M, R, CPL, KSPLIT, PRE>": activation
- * rows, rows per lane, 16-byte chunks per lane per K-tile, waves sharing a row,
- * chunk slots whose loads are issued before the activations are staged).
+ * profilers report it ("qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH>":
+ * activation rows, rows per lane, 16-byte chunks per lane per K-tile, waves
+ * sharing a row, chunk slots whose loads are issued before the activations are
+ * staged, chunk slots in flight per lane).
  * "" when the arguments are invalid.  The string lives in thread-local storage
  * and stays valid until the next call on the same thread.
  */

@@ -162,6 +162,106 @@ def kernel_durations(torch, w4, stack, layers: int, reps: int = 10):
     return out
 
 
+def config_timings(torch, w4, reps: int = 5):
+    """Per-call time of the tiny, LM-head, square and routed configurations,
+    cold: C copies of each matrix (codes xor-ed per copy on device, scales and
+    biases copied) are rotated so that consecutive calls never share weights and
+    one pass over the copies exceeds the 256 MB last-level cache.  Each call
+    sequence is one HIP graph replayed between two events."""
+    out = {}
+
+    def upload(w, copies, shape=None):
+        qw0 = torch.from_numpy(w.qw.view(np.int32)).cuda()
+        s0 = torch.from_numpy(w.scales.view(np.int16)).view(torch.bfloat16).cuda()
+        b0 = torch.from_numpy(w.biases.view(np.int16)).view(torch.bfloat16).cuda()
+        if shape is not None:
+            qw0, s0, b0 = qw0.view(shape[0]), s0.view(shape[1]), b0.view(shape[1])
+        qw = torch.empty((copies,) + tuple(qw0.shape), dtype=torch.int32, device="cuda")
+        sc = torch.empty((copies,) + tuple(s0.shape), dtype=torch.bfloat16, device="cuda")
+        bi = torch.empty_like(sc)
+        for c in range(copies):
+            key = np.array([(0x9E3779B9 * c) & 0xFFFFFFFF], dtype=np.uint32).view(np.int32)[0]
+            qw[c] = qw0 ^ int(key)
+            sc[c] = s0
+            bi[c] = b0
+        del qw0, s0, b0
+        torch.cuda.synchronize()
+        return qw, sc, bi
+
+    def timed(calls, nbytes):
+        g = capture(torch, lambda: [c() for c in calls])
+        ms = time_graph(torch, g, reps, 2)
+        del g
+        us = ms * 1e3 / len(calls)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return dict(us=round(us, 3), gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_GBS, 4))
+
+    # tiny qmv (latency-bound; reported for completeness)
+    t = synthetic.TINY
+    w = synthetic.quantized_weights(t["N"], t["K"], seed=0)
+    qw, sc, bi = upload(w, 8)
+    x = torch.from_numpy(synthetic.activations(1, t["K"], seed=0).view(np.int16)).view(torch.bfloat16).cuda()
+    y = torch.empty((1, t["N"]), dtype=torch.bfloat16, device="cuda")
+    calls = [lambda c=c: w4.w4a16_matmul(x, qw[c], sc[c], bi[c], y) for c in range(8)]
+    out["tiny"] = {"1": timed(calls, call_bytes(1, t["N"], t["K"]))}
+    del qw, sc, bi
+    log(f"tiny: {out['tiny']}")
+
+    # tied LM head with fused argmax (bf16 logits and int32 argmax written)
+    t = synthetic.LM_HEAD
+    N, K = t["N"], t["K"]
+    w = synthetic.quantized_weights(N, K, seed=0, tag=(N,), bias="exact")
+    qw, sc, bi = upload(w, 3)
+    del w
+    out["lm_head"] = {}
+    for M in t["M"]:
+        x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(N,)).view(np.int16)).view(torch.bfloat16).cuda()
+        logits = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        am = torch.empty((M,), dtype=torch.int32, device="cuda")
+        ws = torch.empty((w4.w4a16_lmhead_argmax_workspace_bytes(M, N, K),), dtype=torch.uint8, device="cuda")
+        calls = [lambda c=c: w4.w4a16_lmhead_argmax(x, qw[c], sc[c], bi[c], logits, am, ws)
+                 for c in (0, 1, 2, 0, 1, 2)]
+        out["lm_head"][str(M)] = timed(calls, call_bytes(M, N, K) + 4 * M)
+    del qw, sc, bi
+    log(f"lm_head: {out['lm_head']}")
+
+    # square qmv / qmm
+    t = synthetic.SQUARE
+    N, K = t["N"], t["K"]
+    w = synthetic.quantized_weights(N, K, seed=0, tag=(N,))
+    qw, sc, bi = upload(w, 8)
+    del w
+    out["square"] = {}
+    for M in t["M"]:
+        x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(N,)).view(np.int16)).view(torch.bfloat16).cuda()
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        calls = [lambda c=c: w4.w4a16_matmul(x, qw[c], sc[c], bi[c], y) for c in range(8)]
+        out["square"][str(M)] = timed(calls, call_bytes(M, N, K))
+    del qw, sc, bi
+    log(f"square: {out['square']}")
+
+    # routed MoE stack: 64 experts, top-8 of 64 per token
+    t = synthetic.MOE
+    E, N, K, top_k = t["E"], t["N"], t["K"], t["top_k"]
+    w = synthetic.quantized_weights(E * N, K, seed=0, tag=(E,))
+    qw, sc, bi = upload(w, 3, shape=((E, N, K // 8), (E, N, K // 64)))
+    del w
+    out["moe"] = {}
+    for M in t["M"]:
+        ids_h = synthetic.expert_ids(M, top_k, E, seed=0)
+        ids = torch.from_numpy(ids_h).cuda()
+        x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(E,)).view(np.int16)).view(torch.bfloat16).cuda()
+        y = torch.empty((M, top_k, N), dtype=torch.bfloat16, device="cuda")
+        calls = [lambda c=c: w4.w4a16_matmul_id(x, qw[c], sc[c], bi[c], ids, y) for c in (0, 1, 2, 0, 1, 2)]
+        U = len(np.unique(ids_h))
+        nbytes = U * (N * K // 2 + N * (K // 64) * 4) + 2 * M * K + 2 * M * top_k * N + 4 * M * top_k
+        out["moe"][str(M)] = dict(timed(calls, nbytes), experts=U)
+    del qw, sc, bi
+    log(f"moe: {out['moe']}")
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(host0, seconds: float = 10.0):
     """The oracle, as it stands, on one host core over layer 0's projections."""
     import oracle
@@ -195,6 +295,8 @@ def main():
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-call timings of the tiny, LM-head, square and routed configurations")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy (a known-size reference for "
@@ -271,6 +373,8 @@ def main():
                     per_launch_frac={u: round(unit_bytes(1, unit_ps[u]) / (v * 1e-6) / 1e9 / PEAK_GBS, 4)
                                      for u, v in dur.items()})
 
+    configs = None if args.no_configs else config_timings(torch, w4)
+
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -310,6 +414,7 @@ def main():
                                 cost_vs_m1=round(r["ms"] / r1["ms"], 4))
                    for M, r in results.items() if M != 1},
         "roofline": roofline,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

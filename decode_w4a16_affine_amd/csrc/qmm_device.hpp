@@ -154,27 +154,27 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
   }
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
-    float xv[M][8];
+    // dequantize this word of every row first, then stream the activation rows
+    // through it one at a time (each accumulator still sees its eight products
+    // in ascending k; only the interleaving across accumulators changes)
+    float q[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t word = wd == 0 ? w[r].x : wd == 1 ? w[r].y : wd == 2 ? w[r].z : w[r].w;
+      if (FAST)
+        dequant8_fast(word, s24[r], s20[r], b[r], q[r]);
+      else
+        dequant8_plain(word, s[r], b[r], q[r]);
+    }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float4 lo = xc[(m * 8 + 2 * wd) * PS];
       const float4 hi = xc[(m * 8 + 2 * wd + 1) * PS];
-      xv[m][0] = lo.x; xv[m][1] = lo.y; xv[m][2] = lo.z; xv[m][3] = lo.w;
-      xv[m][4] = hi.x; xv[m][5] = hi.y; xv[m][6] = hi.z; xv[m][7] = hi.w;
-    }
+      const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t word = wd == 0 ? w[r].x : wd == 1 ? w[r].y : wd == 2 ? w[r].z : w[r].w;
-      float q[8];
-      if (FAST)
-        dequant8_fast(word, s24[r], s20[r], b[r], q);
-      else
-        dequant8_plain(word, s[r], b[r], q);
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[r][m] = __builtin_fmaf(xv[m][i], q[i], acc[r][m]);
-      }
+        for (int i = 0; i < 8; ++i) acc[r][m] = __builtin_fmaf(xv[i], q[r][i], acc[r][m]);
     }
   }
 }

@@ -48,7 +48,7 @@ struct Sched;
 template <int M, int CLS>
 struct Sched<M, 1, CLS> {
   static constexpr int R = (CLS & 1) && M <= 5 ? 2 : 1;
-  static constexpr int CPL = M <= 3 ? ((CLS & 2) ? 5 : 4) : (((CLS & 2) && R == 1) ? 5 : 3);
+  static constexpr int CPL = M <= 3 ? ((CLS & 2) ? 5 : 4) : (R == 1 ? ((CLS & 2) ? 5 : 4) : 3);
   static constexpr int PRE = 1;
   static constexpr int DEPTH = (R == 2 && M == 1) ? 3 : 2;
 };
@@ -322,22 +322,39 @@ __global__ __launch_bounds__(kThreads) void qmm_stream_kernel(const uint16_t* __
   }
 }
 
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* __restrict__ partial, int nblocks, int M,
-                                                              int32_t* __restrict__ argmax) {
-  __shared__ uint64_t s[256];
+// Final argmax over the per-block keys of one activation row (blockIdx.x).
+// Every thread keeps eight independent loads in flight per round, so the
+// reduction costs one or two memory round trips rather than one per key; the
+// max of distinct keys does not depend on the order of combination.
+constexpr int kFinalThreads = 1024;
+__global__ __launch_bounds__(kFinalThreads) void argmax_finalize_kernel(const uint64_t* __restrict__ partial,
+                                                                        int nblocks, int M,
+                                                                        int32_t* __restrict__ argmax) {
+  __shared__ uint64_t s[kFinalThreads / kWave];
   const int m = blockIdx.x;
   uint64_t best = 0;
-  for (int i = threadIdx.x; i < nblocks; i += 256) {
-    const uint64_t k = partial[(size_t)i * M + m];
-    best = k > best ? k : best;
+  for (int i0 = threadIdx.x; i0 < nblocks; i0 += kFinalThreads * 8) {
+    uint64_t k[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kFinalThreads;
+      k[u] = i < nblocks ? partial[(size_t)i * M + m] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) best = k[u] > best ? k[u] : best;
   }
-  s[threadIdx.x] = best;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(best, off);
+    best = o > best ? o : best;
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) s[threadIdx.x / kWave] = best;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) s[threadIdx.x] = s[threadIdx.x + w] > s[threadIdx.x] ? s[threadIdx.x + w] : s[threadIdx.x];
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kFinalThreads / kWave; ++w) best = s[w] > best ? s[w] : best;
+    best = s[0] > best ? s[0] : best;
+    argmax[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
   }
-  if (threadIdx.x == 0) argmax[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)(s[0] & 0xFFFFFFFFull));
 }
 
 // One pass of the routed product: C slots routed to one expert.
@@ -388,27 +405,40 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(const
     }
     return;
   }
-  for (int j = 0; j < slot; ++j)
-    if (ids[j] == e) return;  // an earlier slot streams this expert
+  // An earlier slot routed to e streams the expert for all of them.  The ids
+  // are read 64 at a time, one per lane, and compared with a ballot: one
+  // memory round trip per 64 slots instead of one per slot.
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int base = 0; base < slot; base += kWave) {
+    const int j = base + lane;
+    const int v = j < slot ? ids[j] : -1;
+    if (__ballot(v == e)) return;
+  }
   const size_t wpr = (size_t)(K >> 3);
   const size_t gpr = (size_t)(K >> 6);
   const RowSrc src{qw + (size_t)e * N * wpr, scales + (size_t)e * N * gpr, biases + (size_t)e * N * gpr, N, K};
-  int j = slot;
-  while (j < nslots) {
-    int list[MB];
-    int cnt = 0;
-    for (; j < nslots && cnt < MB; ++j)
-      if (ids[j] == e) list[cnt++] = j;
-    if (cnt == 0) break;
-    switch (cnt) {
-      case 1: routed_pass<1, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 4: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 5: if constexpr (MB >= 5) routed_pass<5, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 6: if constexpr (MB >= 6) routed_pass<6, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      case 7: if constexpr (MB >= 7) routed_pass<7, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-      default: if constexpr (MB >= 8) routed_pass<8, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+  // The slots routed to e, ascending, in passes of at most MB activation rows;
+  // each pass takes the lowest set bits of the current 64-slot ballot, so the
+  // row bodies are instantiated at one call site.
+  for (int base = slot; base < nslots; base += kWave) {
+    const int j = base + lane;
+    const int v = j < nslots ? ids[j] : -1;
+    uint64_t m = __ballot(v == e);
+    while (m) {
+      int list[MB];
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        list[u] = m ? base + (int)__builtin_ctzll(m) : list[0];
+        cnt += m ? 1 : 0;
+        m &= m - 1;
+      }
+      switch (cnt) {
+        case 1: routed_pass<1, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+        case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+        case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+        default: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+      }
     }
   }
 }
@@ -745,8 +775,7 @@ w4a16_status_t w4a16_matmul_id(const uint16_t* x, int x_per_slot, const uint32_t
   // Without duplicate ids in a token, an expert serves at most M slots.
   if (M == 1) return launched(routed_by_split<1>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
   if (M == 2) return launched(routed_by_split<2>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
-  if (M <= 4) return launched(routed_by_split<4>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
-  return launched(routed_by_split<8>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
+  return launched(routed_by_split<4>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
 }
 
 size_t w4a16_lmhead_argmax_workspace_bytes(int M, int N, int K, int group) {
@@ -785,7 +814,7 @@ w4a16_status_t w4a16_lmhead_argmax(const uint16_t* x, const uint32_t* qw, const 
     default: e = lmhead_by_split<8>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
   }
   if (e != hipSuccess) return W4A16_ERR_HIP;
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(256), 0, s, partial, nb, M, argmax);
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(kFinalThreads), 0, s, partial, nb, M, argmax);
   return launched(hipGetLastError());
 }
 

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
                                                               uint64_t* __restrict__ partial, int N, int K) {
   __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
-  __shared__ uint64_t keys[kBlockWaves<KSPLIT> * kSlots][M];
+  __shared__ uint64_t keys[kBlockWaves<KSPLIT>][M];
   using RM = RowMap<R, KSPLIT>;
   XRows<M> xr;
   size_t yoff[M];
@@ -204,33 +204,41 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
   block_rows<M, R, CPL, KSPLIT, PRE, DEPTH>(acc, xr, src, block_row0, xs, red);
   if (logits) store_to<M, R, KSPLIT>(acc, row_first, N, logits, yoff, out_f32 != 0);
 
+  // Block maximum of the (value, index) keys: every lane of a row group holds
+  // its rows' sums, so a wave reduces its four row groups with two 64-bit
+  // shuffles, then one key per wave goes through LDS.  (With a K-split all
+  // waves hold the same rows; wave 0's keys are the block's.)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int t = lane & (kRowLanes - 1);
-  const int slot = lane / kRowLanes;
-  if (t == 0) {
+  uint64_t best[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      uint64_t best = 0;
+  for (int m = 0; m < M; ++m) {
+    best[m] = 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int n = row_first + r;
-        if (n < N) {
-          const uint64_t k = argmax_key(acc[r][m], (uint32_t)n);
-          best = k > best ? k : best;
-        }
-      }
-      keys[wave * kSlots + slot][m] = (KSPLIT == 1 || wave == 0) ? best : 0;
+    for (int r = 0; r < R; ++r) {
+      const int n = row_first + r;
+      const uint64_t k = n < N ? argmax_key(acc[r][m], (uint32_t)n) : 0;
+      best[m] = k > best[m] ? k : best[m];
     }
+    uint64_t o = __shfl_xor(best[m], kRowLanes);
+    best[m] = o > best[m] ? o : best[m];
+    o = __shfl_xor(best[m], 2 * kRowLanes);
+    best[m] = o > best[m] ? o : best[m];
+  }
+  constexpr int kKeyWaves = KSPLIT == 1 ? kBlockWaves<KSPLIT> : 1;
+  if (lane == 0 && wave < kKeyWaves) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) keys[wave][m] = best[m];
   }
   __syncthreads();
   if (threadIdx.x < M) {
-    uint64_t best = 0;
-    for (int i = 0; i < kBlockWaves<KSPLIT> * kSlots; ++i) {
+    uint64_t b = keys[0][threadIdx.x];
+#pragma unroll
+    for (int i = 1; i < kKeyWaves; ++i) {
       const uint64_t k = keys[i][threadIdx.x];
-      best = k > best ? k : best;
+      b = k > b ? k : b;
     }
-    partial[(size_t)blockIdx.x * M + threadIdx.x] = best;
+    partial[(size_t)blockIdx.x * M + threadIdx.x] = b;
   }
 }
 

@@ -14,6 +14,9 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     # no packed fp32 arithmetic (v_pk_fma_f32 and friends) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 16 kernel-argument dwords arrive in scalar registers at wave
+    # launch (gfx950 argument preloading; older firmware runs a load prologue)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -126,10 +126,12 @@ __device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first
 
 // Up to kMaxMats matrices that share K and the activations, launched together:
 // grid row blockIdx.y streams matrix blockIdx.y, and blocks past that matrix's
-// rows exit at once.  MatList is the host-side list; the kernel receives
-// MatArgs, the same fields as arrays indexed by blockIdx.y, so that every
-// field the block needs is one kernel-argument load at an offset known at
-// wave start (no chain of dependent scalar loads before the first weight load).
+// rows exit at once.  MatList is the host-side list.  The kernel receives the
+// first matrix as plain arguments that, with x, N, K and the output type, fit
+// the 16 argument dwords the hardware can preload into scalar registers at
+// wave launch (no memory round trip before the first weight load); the other
+// matrices come as arrays indexed by blockIdx.y - 1 (MatArgs), one
+// kernel-argument load each.
 constexpr int kMaxMats = 8;
 static_assert(kMaxMats >= W4A16_MAX_GROUP, "a grouped launch must hold every matrix of a call");
 struct MatDesc {
@@ -144,24 +146,25 @@ struct MatList {
   int count;
 };
 struct MatArgs {
-  const uint32_t* qw[kMaxMats];
-  const uint16_t* scales[kMaxMats];
-  const uint16_t* biases[kMaxMats];
-  void* y[kMaxMats];
-  int N[kMaxMats];
+  const uint32_t* qw[kMaxMats - 1];
+  const uint16_t* scales[kMaxMats - 1];
+  const uint16_t* biases[kMaxMats - 1];
+  void* y[kMaxMats - 1];
+  int N[kMaxMats - 1];
 };
 
 template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
-__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(const uint16_t* __restrict__ x,
-                                                                          const MatArgs mats, int out_f32, int K) {
+__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
+    int N0, int K, int out_f32, const MatArgs more) {
   __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
   using RM = RowMap<R, KSPLIT>;
-  const int mi = blockIdx.y;
-  MatDesc d{mats.qw[mi], mats.scales[mi], mats.biases[mi], mats.y[mi], mats.N[mi]};
-  // one asm that consumes every argument: all of their loads are issued before
-  // the first wait, instead of being sunk one by one to their first use
-  asm volatile("" ::"s"(d.qw), "s"(d.scales), "s"(d.biases), "s"(d.y), "s"(d.N), "s"(x), "s"(K), "s"(out_f32));
+  MatDesc d{qw0, scales0, biases0, y0, N0};
+  if (blockIdx.y > 0) {
+    const int mi = blockIdx.y - 1;
+    d = MatDesc{more.qw[mi], more.scales[mi], more.biases[mi], more.y[mi], more.N[mi]};
+  }
   const int block_row0 = (int)blockIdx.x * RM::kRowsPerBlock;
   if (block_row0 >= d.N) return;   // uniform per block: before any barrier
   XRows<M> xr;
@@ -385,13 +388,12 @@ __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, 
 }
 
 template <int MB, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
-__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(const uint16_t* __restrict__ x, int x_per_slot,
-                                                              const uint32_t* __restrict__ qw,
-                                                              const uint16_t* __restrict__ scales,
-                                                              const uint16_t* __restrict__ biases,
-                                                              const int32_t* __restrict__ ids, void* __restrict__ y,
-                                                              int out_f32, int M, int top_k, int E, int N, int K,
-                                                              int tiles) {
+// (Arguments ordered so that what a block needs before its first memory access
+// sits in the 16 dwords the hardware preloads into scalar registers.)
+__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, const int32_t* __restrict__ ids, void* __restrict__ y, int N, int K,
+    int tiles, int M, int top_k, int E, int x_per_slot, int out_f32) {
   __shared__ float4 xs[MB * 8 * CPL * kRowLanes * KSPLIT];
   __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * MB];
   using RM = RowMap<R, KSPLIT>;
@@ -527,15 +529,17 @@ hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, 
   for (int i = 0; i < ml.count; ++i) {
     const long bi = (ml.m[i].N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
     blocks = bi > blocks ? bi : blocks;
-    a.qw[i] = ml.m[i].qw;
-    a.scales[i] = ml.m[i].scales;
-    a.biases[i] = ml.m[i].biases;
-    a.y[i] = ml.m[i].y;
-    a.N[i] = ml.m[i].N;
+    if (i == 0) continue;
+    a.qw[i - 1] = ml.m[i].qw;
+    a.scales[i - 1] = ml.m[i].scales;
+    a.biases[i - 1] = ml.m[i].biases;
+    a.y[i - 1] = ml.m[i].y;
+    a.N[i - 1] = ml.m[i].N;
   }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  const MatDesc& m0 = ml.m[0];
   hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH>), dim3((unsigned)blocks, (unsigned)ml.count),
-                     dim3(kBlockThreads<KSPLIT>), 0, st, x, a, out_f32, K);
+                     dim3(kBlockThreads<KSPLIT>), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a);
   return hipGetLastError();
 }
 
@@ -634,7 +638,7 @@ hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, 
   if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
   hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH>), dim3((unsigned)blocks),
                      dim3(kBlockThreads<KSPLIT>), 0, st,
-                     x, x_per_slot, qw, s, b, ids, y, out_f32, M, top_k, E, N, K, tiles);
+                     x, qw, s, b, ids, y, N, K, tiles, M, top_k, E, x_per_slot, out_f32);
   return hipGetLastError();
 }
 

@@ -35,6 +35,10 @@ import synthetic  # noqa: E402
 METRIC = "achieved HBM GB/s (% of MI355X peak) for W4A16 qmv M=1 and qmm M=k+1"
 PEAK_GBS = 8000.0
 LAYERS = 42
+# untimed replay time before each measurement (beyond the warm-up count): the
+# first measurement runs the step for a second so the clocks have settled
+FIRST_WARM_S = 1.0
+WARM_S = 0.25
 
 
 def call_bytes(M: int, N: int, K: int) -> int:
@@ -131,10 +135,18 @@ def capture(torch, fn):
     return g
 
 
-def time_graph(torch, g, steps: int, warmup: int) -> float:
+def time_graph(torch, g, steps: int, warmup: int, min_warm_s: float = 0.0) -> float:
+    """Replay `warmup` times, and further until `min_warm_s` seconds of replays
+    have run (the GPU's clocks settle only after some tenths of a second of
+    load), then time `steps` replays between two events."""
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     # graph replays run on the current stream, where the events are recorded
@@ -157,7 +169,7 @@ def kernel_durations(torch, w4, stack, layers: int, reps: int = 10):
     for u, ps in UNITS_GROUPED + tuple(x for x in UNITS_SEPARATE if x[0] in ("q", "k", "v")):
         units = UNITS_GROUPED if u in dict(UNITS_GROUPED) else UNITS_SEPARATE
         g = capture(torch, make_step(w4, stack, 1, layers, units=units, only=(u,)))
-        out[u] = time_graph(torch, g, reps, 2) * 1e3 / layers
+        out[u] = time_graph(torch, g, reps, 2, WARM_S) * 1e3 / layers
         del g
     return out
 
@@ -190,7 +202,7 @@ def config_timings(torch, w4, reps: int = 5):
 
     def timed(calls, nbytes):
         g = capture(torch, lambda: [c() for c in calls])
-        ms = time_graph(torch, g, reps, 2)
+        ms = time_graph(torch, g, reps, 2, WARM_S)
         del g
         us = ms * 1e3 / len(calls)
         gbs = nbytes / (us * 1e-6) / 1e9
@@ -325,13 +337,13 @@ def main():
         g = capture(torch, make_step(w4, stack, M, L))
         steps = args.steps if M == 1 else max(10, args.steps // 2)
         warm = args.warmup if M == 1 else max(3, args.warmup // 2)
-        ms = time_graph(torch, g, steps, warm)
+        ms = time_graph(torch, g, steps, warm, FIRST_WARM_S if M == 1 else WARM_S)
         nb = step_bytes(M, L)
         results[M] = dict(ms=ms, gbs=nb / (ms * 1e-3) / 1e9, bytes=nb, steps=steps, warmup=warm)
         log(f"M={M}: {ms:.4f} ms/step, {results[M]['gbs']:.1f} GB/s")
         del g
     g = capture(torch, make_step(w4, stack, 1, L, units=UNITS_SEPARATE))
-    ms_sep = time_graph(torch, g, args.steps, args.warmup)
+    ms_sep = time_graph(torch, g, args.steps, args.warmup, WARM_S)
     del g
     log(f"M=1, six launches per layer: {ms_sep:.4f} ms/step")
 

@@ -307,6 +307,9 @@ def main():
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--warm-seconds", type=float, default=None,
+                    help="untimed replay time before each measurement (default: 1 s before the first, "
+                         "0.25 s before the others; profiler runs use 0)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-call timings of the tiny, LM-head, square and routed configurations")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -314,6 +317,9 @@ def main():
                     help="also run a 256 MiB device-to-device copy (a known-size reference for "
                          "memory-traffic counters)")
     args = ap.parse_args()
+    global FIRST_WARM_S, WARM_S
+    if args.warm_seconds is not None:
+        FIRST_WARM_S = WARM_S = max(0.0, args.warm_seconds)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(a multi-GPU deployment would shard output rows or experts; this benchmark runs on one)", file=sys.stderr)

@@ -179,6 +179,26 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
   }
 }
 
+// Chunk slot j of a tile against the staged activations at xc: the bf16
+// scale and bias become fp32 (exact), and the wave takes the plain dequant path
+// for the chunk if any of its lanes holds a scale too large for the fast one.
+template <int M, int R, int PS, int CPL>
+__device__ __forceinline__ void consume_slot(float (&acc)[R][M], const Tile<CPL, R>& tl, int j,
+                                             const float4* xc) {
+  float s[R], b[R];
+  bool plain = false;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    s[r] = __uint_as_float(tl.s[j][r] << 16);
+    b[r] = __uint_as_float(tl.b[j][r] << 16);
+    plain |= needs_plain(s[r]);
+  }
+  if (__any(plain))
+    chunk_fma<M, R, PS, false>(acc, tl.w[j], s, b, xc);
+  else
+    chunk_fma<M, R, PS, true>(acc, tl.w[j], s, b, xc);
+}
+
 // Per-wave view of the rows being streamed: buffer resources that end at the
 // last real row (loads of rows >= N return zero), words and groups per row,
 // and this lane's place in the row (L) and in the wave (slot).
@@ -189,6 +209,24 @@ struct WaveRows {
   int L;          // lane index within the row's LPR lanes
   int slot;       // row group within the wave
 };
+
+// Activations of one K-tile as fp32 in LDS.  Layout (float4 units):
+// xs[(m * 8 + piece) * CS + c] holds k = k0 + 32c + 4 piece .. +3.  Threads past
+// the end repeat the last piece (same value, same address).
+template <int M, int XL, int NT, int CS>
+__device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, float4* xs) {
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = min((int)threadIdx.x + j * NT, xq - 1);
+      const int kk = 8 * i;
+      const int c = kk >> 5, piece = (kk >> 2) & 7;
+      const uint4 v = xv[m][j];
+      xs[(m * 8 + piece) * CS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+      xs[(m * 8 + piece + 1) * CS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+    }
+}
 
 // One K-tile [k0, k0 + klen) of the R rows of this lane's row group.
 // FULL: klen equals the tile size, so every chunk slot of every lane is in
@@ -294,6 +332,108 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
   }
 }
 
+// Activation tiles are double-buffered in LDS (see rolled_tiles) when both
+// buffers stay within 32 KiB per block, i.e. four blocks still fit on a CU.
+template <int M, int CPL, int KSPLIT>
+constexpr bool kRolled = KSPLIT == 1 && 2 * M * 8 * CPL * kRowLanes * 16 <= 32768;
+// float4 of LDS a block needs for its activation tiles
+template <int M, int CPL, int KSPLIT>
+constexpr int kXsF4 = M * 8 * CPL * kRowLanes * KSPLIT * (kRolled<M, CPL, KSPLIT> ? 2 : 1);
+
+// The first `ntiles` (>= 2) full K-tiles of the rows, without a K-split, as one
+// software pipeline: the chunk slots form a single stream across tile
+// boundaries (when slot j of tile t is consumed, the load of slot j + DEPTH goes
+// out, into the next tile when j + DEPTH >= CPL), and tile t + 1's activations
+// are loaded during tile t and staged into the other LDS buffer at its end, so
+// one barrier per tile remains and the weight stream never drains between
+// tiles.  Loads are never conditional (past the last tile they use an offset
+// outside the resource, or repeat the last activation tile), so the compiler's
+// vmcnt waits stay chunk-exact.  Every lane consumes the same chunks in the same
+// order with the same body as tile_pass: the sums are bitwise those of the
+// tile-by-tile walk.  xs must hold 2 * M * 8 * CPL * 16 float4.
+template <int M, int R, int CPL, int PRE, int DEPTH>
+__device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w,
+                                             int ntiles, float4* xs) {
+  constexpr int LPR = kRowLanes;
+  constexpr int CS = CPL * LPR;                               // chunks per K-tile
+  constexpr int KTILE = CS * 32;                              // codes per K-tile
+  constexpr int NT = kBlockThreads<1>;
+  constexpr int XQ = KTILE / 8;                               // 16-byte x pieces per row per tile
+  constexpr int XL = (XQ + NT - 1) / NT;
+  constexpr int XBUF = M * 8 * CS;                            // float4 per activation buffer
+  constexpr int D = DEPTH < CPL ? DEPTH : CPL;
+  constexpr int P0 = PRE < D ? PRE : D;
+  const int L = w.L;
+
+  uint4 xv[M][XL];
+  auto x_issue = [&](int t) {
+    const int tt = min(t, ntiles - 1);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        const int i = min((int)threadIdx.x + j * NT, XQ - 1);
+        xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + tt * KTILE)[i];
+      }
+  };
+
+  Tile<CPL, R> tl;
+  uint32_t qb[R], gb[R];    // byte offsets of chunk slot 0 of the current tile
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t lr = (uint32_t)(w.slot * R + r);
+    qb[r] = lr * w.wpr * 4u + (uint32_t)L * 16u;
+    gb[r] = lr * w.gpr * 2u + (uint32_t)(L >> 1) * 2u;
+  }
+  // slot j of the current tile (NEXT: of the following tile; none past the last)
+  auto load = [&](int j, bool next, bool live) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t step = (uint32_t)((next ? CS : 0) + j * LPR);
+      const uint32_t oq = live ? qb[r] + step * 16u : kOffNone;
+      const uint32_t og = live ? gb[r] + step : kOffNone;
+      tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, 0));
+      tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
+      tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
+    }
+  };
+
+  x_issue(0);
+#pragma unroll
+  for (int j = 0; j < P0; ++j) load(j, false, true);
+  __syncthreads();   // the block is done with any earlier contents of xs
+  x_stage_tile<M, XL, NT, CS>(xv, XQ, xs);
+  x_issue(1);
+  __syncthreads();
+#pragma unroll
+  for (int j = P0; j < D; ++j) load(j, false, true);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const float4* xb = xs + (t & 1) * XBUF;
+    const bool more = t + 1 < ntiles;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      // the load that keeps D slots in flight: slot j + D of this tile, or slot
+      // j + D - CPL of the next one (whose registers were consumed already, or
+      // are consumed right now when D == CPL: then it goes out afterwards)
+      if (j + D < CPL) load(j + D, false, true);
+      else if (j + D - CPL < j) load(j + D - CPL, true, more);
+      consume_slot<M, R, CS>(acc, tl, j, xb + L + j * LPR);
+      if (j + D >= CPL && j + D - CPL == j) load(j, true, more);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      qb[r] += (uint32_t)CS * 16u;
+      gb[r] += (uint32_t)CS;
+    }
+    // tile t + 1's activations into the other buffer (last read during tile
+    // t - 1, which every wave finished before the previous barrier)
+    x_stage_tile<M, XL, NT, CS>(xv, XQ, xs + ((t + 1) & 1) * XBUF);
+    x_issue(t + 2);
+    __syncthreads();
+  }
+}
+
 // Full-row sums for the R rows of this lane's row group.
 //
 // Lane L of a row (L = t without K-split, wave*16 + t with one) owns the
@@ -307,7 +447,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 // KSPLIT == 1: on return every lane of the row group holds the sums.
 // KSPLIT == S > 1: the S waves of the block share the rows; on return every
 //              lane of every wave holds the sums (combined in wave order).
-// xs must hold M * 8 * CPL * LPR float4.  Call with all threads (barriers).
+// xs must hold kXsF4<M, CPL, KSPLIT> float4.  Call with all threads (barriers).
 template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
@@ -336,7 +476,15 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-  for (int k0 = 0; k0 < K; k0 += KTILE) {
+  int kr = 0;
+  if constexpr (kRolled<M, CPL, KSPLIT>) {
+    const int nfull = K / KTILE;
+    if (nfull >= 2) {
+      rolled_tiles<M, R, CPL, PRE, DEPTH>(acc, xr, w, nfull, xs);
+      kr = nfull * KTILE;
+    }
+  }
+  for (int k0 = kr; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
     if (klen == KTILE)
       tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true>(acc, xr, w, k0, klen, xs);

@@ -33,11 +33,18 @@ int ksplit_for(int N, int K) {
 
 // Schedules measured on MI355X (cold weights, graph-replayed launches).
 //
-// KSPLIT 1 classes (bit 0: very tall matrices, N >= 131072, vocabulary heads,
-// where two rows per lane win; bit 1: K a multiple of 2560 but not of 2048, so
-// tiles of 5 chunks per lane cover K exactly, otherwise 4): tiles that cover K
-// exactly use straight-line loads with immediate offsets.
+// KSPLIT 1 classes: bit 0: vocabulary heads (N >= 131072); bit 1: K a multiple
+// of 2560 but not of 2048, so tiles of 5 chunks per lane cover K exactly
+// (otherwise 4); bit 2: tall matrices (N >= 16384), where two rows per lane
+// win once M >= 2 (the activation reads from LDS, 4M bytes per weight and lane,
+// halve; with N >= 16384 the grid still holds 8 waves per CU).  Tiles that
+// cover K exactly use straight-line loads with immediate offsets.  For M >= 6
+// the activation tile of a 5-chunk K-tile alone (M * 10 KiB per block) would
+// cap the CU at two blocks, so those rows take 2-chunk tiles.
 // KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile.
+// KSPLIT 5: one chunk per lane; two rows per lane from M = 2 (in the grouped
+// q/k/v launch, one row per lane doubles the blocks and cost 1.2-2 us per
+// launch at M = 2..5).
 // PRE: chunk slots whose loads go out before the activations are staged (the
 // rest follow the staging barrier, so the activation loads are not queued
 // behind the whole tile).  DEPTH: chunk slots in flight per lane; later slots
@@ -47,15 +54,20 @@ template <int M, int KSPLIT, int CLS>
 struct Sched;
 template <int M, int CLS>
 struct Sched<M, 1, CLS> {
-  static constexpr int R = (CLS & 1) && M <= 5 ? 2 : 1;
-  static constexpr int CPL = M <= 3 ? ((CLS & 2) ? 5 : 4) : (R == 1 ? ((CLS & 2) ? 5 : 4) : 3);
+  static constexpr bool kHead = (CLS & 1) != 0, k2560 = (CLS & 2) != 0, kTall = (CLS & 4) != 0;
+  static constexpr int R = M == 1 ? (kHead ? 2 : 1) : !kTall ? 1 : (k2560 && M <= 3 && !kHead) ? 1 : 2;
+  static constexpr int CPL = !kTall || M == 1 ? (k2560 ? 5 : 4)
+                             : !k2560 ? 4
+                             : M <= 3 ? 5
+                             : M <= 5 ? (kHead ? 3 : 5)
+                             : 2;
   static constexpr int PRE = 1;
   static constexpr int DEPTH = (R == 2 && M == 1) ? 3 : 2;
 };
 template <int M, int CLS>
 struct Sched<M, 4, CLS> {
   static constexpr int R = (CLS == 1 && M >= 3) ? 2 : 1;
-  static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 && R == 1 ? 2 : 1);
+  static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 ? 2 : 1);
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 2;
 };
@@ -70,7 +82,7 @@ struct Sched<M, 5, CLS> {
 int sched_class(int N, int K, int ksplit) {
   if (ksplit == 5) return 0;
   if (ksplit == 4) return K > 4096;
-  return (N >= 131072 ? 1 : 0) | (K % 2048 != 0 && K % 2560 == 0 ? 2 : 0);
+  return (N >= 131072 ? 1 : 0) | (K % 2048 != 0 && K % 2560 == 0 ? 2 : 0) | (N >= 16384 ? 4 : 0);
 }
 
 // Calls f(integral_constant<KSPLIT>, integral_constant<CLS>) for a runtime (ksplit, cls).
@@ -81,10 +93,12 @@ auto with_sched(int ksplit, int cls, F&& f) {
   if (ksplit == 4)
     return cls ? f(integral_constant<int, 4>{}, integral_constant<int, 1>{})
                : f(integral_constant<int, 4>{}, integral_constant<int, 0>{});
-  switch (cls) {
-    case 1: return f(integral_constant<int, 1>{}, integral_constant<int, 1>{});
+  switch (cls) {   // bit 0 implies bit 2
     case 2: return f(integral_constant<int, 1>{}, integral_constant<int, 2>{});
-    case 3: return f(integral_constant<int, 1>{}, integral_constant<int, 3>{});
+    case 4: return f(integral_constant<int, 1>{}, integral_constant<int, 4>{});
+    case 5: return f(integral_constant<int, 1>{}, integral_constant<int, 5>{});
+    case 6: return f(integral_constant<int, 1>{}, integral_constant<int, 6>{});
+    case 7: return f(integral_constant<int, 1>{}, integral_constant<int, 7>{});
     default: return f(integral_constant<int, 1>{}, integral_constant<int, 0>{});
   }
 }
@@ -157,7 +171,7 @@ template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
 __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(
     const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
     int N0, int K, int out_f32, const MatArgs more) {
-  __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
+  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
   __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
   using RM = RowMap<R, KSPLIT>;
   MatDesc d{qw0, scales0, biases0, y0, N0};
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
                                                               const uint16_t* __restrict__ biases,
                                                               void* __restrict__ logits, int out_f32,
                                                               uint64_t* __restrict__ partial, int N, int K) {
-  __shared__ float4 xs[M * 8 * CPL * kRowLanes * KSPLIT];
+  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
   __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
   __shared__ uint64_t keys[kBlockWaves<KSPLIT>][M];
   using RM = RowMap<R, KSPLIT>;
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const int32_t* __restrict__ ids, void* __restrict__ y, int N, int K,
     int tiles, int M, int top_k, int E, int x_per_slot, int out_f32) {
-  __shared__ float4 xs[MB * 8 * CPL * kRowLanes * KSPLIT];
+  __shared__ float4 xs[kXsF4<MB, CPL, KSPLIT>];
   __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * MB];
   using RM = RowMap<R, KSPLIT>;
   const int nslots = M * top_k;

@@ -130,7 +130,12 @@ def test_decode_projections_and_verify_batches(orc, name):
             assert np.array_equal(yb[m], singlesb[m]), (name, M, m)
 
 
-RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560), (61, 2560), (300, 5120)]
+# (4200, 4672) and (4500, 7680): one row group per row, walked in several
+# K-tiles (two full tiles and a ragged tail; three full tiles: the
+# double-buffered walk); (16400, 576) and (16390, 2560): N >= 16384, where the
+# rows per lane and the tile length change with M
+RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560), (61, 2560), (300, 5120),
+          (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)
@@ -391,6 +396,24 @@ def test_routed_moe_config(orc):
         w4.w4a16_matmul(dev_bf16(x[m:m + 1]), stack[0][e], stack[1][e], stack[2][e], yd)
         torch.cuda.synchronize()
         assert np.array_equal(host_f32(yd)[0].view(np.uint32), y8[m, j].view(np.uint32))
+
+
+def test_routed_long_rows(orc):
+    # experts tall enough for one row group per row and K spanning two full
+    # K-tiles plus a ragged tail
+    E, N, K, M, top_k = 3, 4100, 4288, 3, 2
+    w, x, _ = routed_inputs(E, N, K, M, top_k, seed=21)
+    stack = (dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases))
+    ids = np.array([[0, 2], [1, 0], [2, 1]], dtype=np.int32)
+    say(f"routed long rows E={E} N={N} K={K} M={M}: oracle")
+    y64, absy = orc.qmm_id(x, w.qw, w.scales, w.biases, ids)
+    y = run_id(stack, x, ids, N)
+    check_f32(y, y64, absy, "routed long rows")
+    for m in range(M):
+        say(f"  routed long rows token {m}")
+        y1 = run_id(stack, x[m:m + 1], ids[m:m + 1], N)
+        check_f32(y1, y64[m:m + 1], absy[m:m + 1], f"routed long rows M=1 token {m}")
+        assert np.array_equal(y1[0].view(np.uint32), y[m].view(np.uint32)), m
 
 
 def test_routed_variants(orc):

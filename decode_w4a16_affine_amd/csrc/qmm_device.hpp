@@ -30,7 +30,6 @@ namespace w4k {
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;                      // waves per block without K-split
-constexpr int kThreads = kWave * kWaves;
 constexpr int kRowLanes = 16;
 constexpr int kSlots = kWave / kRowLanes;      // row groups per wave
 
@@ -514,116 +513,6 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
         acc[r][m] = v;
       }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Streaming schedule (persistent waves, software-pipelined).
-//
-// The block stages the activations for the whole of K once, chunk-major:
-// chunk c occupies kXChunk<M> float4, piece p of activation row m at
-// [c * kXChunk<M> + m * 8 + p] (one float4 of padding per chunk keeps the
-// 16 lanes of a row group on distinct banks).  Each wave then walks its own
-// sequence of work items -- (row set of kSlots*R rows, K-tile of CPL chunks per
-// lane) -- with two register sets: the loads of item u+1 are in flight while
-// item u is consumed.  Lane t still owns chunks t, t+16, ... of its rows in
-// ascending order and the chunk body, reduction tree and rounding are those of
-// block_rows, so every output is bitwise the same as the block schedule's.
-// ---------------------------------------------------------------------------
-template <int M>
-constexpr int kXChunk = M * 8 + 1;
-
-struct ItemSrc {
-  __amdgpu_buffer_rsrc_t rq, rs, rb;
-};
-
-// Resources of the item (row set starting at row0, K-tile kt): they start at
-// the tile's first chunk of row0 and end with the last real row of the set, so
-// rows >= N read zero; a missing item (live == false) reads zero everywhere.
-__device__ __forceinline__ ItemSrc item_src(const RowSrc& src, int row0, int kt, int chunks_per_tile,
-                                            int rows_per_set, bool live, uint32_t wpr, uint32_t gpr) {
-  const int rows = live ? max(0, min(rows_per_set, src.N - row0)) : 0;
-  const uint32_t qskip = (uint32_t)kt * (uint32_t)chunks_per_tile * 16u;   // bytes of the row before the tile
-  const uint32_t gskip = (uint32_t)kt * (uint32_t)chunks_per_tile;         // bytes of scales before the tile
-  const uint32_t qbytes = rows > 0 ? (uint32_t)rows * wpr * 4u - qskip : 0u;
-  const uint32_t gbytes = rows > 0 ? (uint32_t)rows * gpr * 2u - gskip : 0u;
-  const size_t r0 = (size_t)(live ? row0 : 0);
-  ItemSrc is;
-  is.rq = make_rsrc(reinterpret_cast<const char*>(src.qw + r0 * wpr) + qskip, qbytes);
-  is.rs = make_rsrc(reinterpret_cast<const char*>(src.scales + r0 * gpr) + gskip, gbytes);
-  is.rb = make_rsrc(reinterpret_cast<const char*>(src.biases + r0 * gpr) + gskip, gbytes);
-  return is;
-}
-
-// Lane offsets inside an item: row slot*R + r, chunk slot j at +j*256 bytes
-// (codes) and +j*16 bytes (scales, biases: two chunks per group, 16 chunks apart).
-template <int R>
-struct LaneOff {
-  uint32_t q[R];
-  uint32_t g[R];
-};
-
-template <int CPL, int R>
-__device__ __forceinline__ void item_issue(Tile<CPL, R>& it, const ItemSrc& is, const LaneOff<R>& lo) {
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      it.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(is.rq, lo.q[r] + j * 256u, 0, 0));
-      it.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(is.rs, lo.g[r] + j * 16u, 0, 0);
-      it.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(is.rb, lo.g[r] + j * 16u, 0, 0);
-    }
-}
-
-// Consume one item; xw points at this lane's first chunk of the tile.
-template <int M, int R, int CPL>
-__device__ __forceinline__ void item_consume(float (&acc)[R][M], const Tile<CPL, R>& it, const float4* xw) {
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    float s[R], b[R];
-    bool plain = false;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      s[r] = __uint_as_float(it.s[j][r] << 16);
-      b[r] = __uint_as_float(it.b[j][r] << 16);
-      plain |= needs_plain(s[r]);
-    }
-    const float4* xc = xw + j * kRowLanes * kXChunk<M>;
-    if (__any(plain))
-      chunk_fma<M, R, 1, false>(acc, it.w[j], s, b, xc);
-    else
-      chunk_fma<M, R, 1, true>(acc, it.w[j], s, b, xc);
-  }
-}
-
-// Stage x[M, K] (bf16) into LDS as fp32 in the chunk-major layout.  XL: 16-byte
-// loads per thread and activation row, XL * kThreads * 8 >= K.  The loads are
-// issued by the caller first (x_load) so that later weight loads do not delay them.
-template <int M, int XL>
-__device__ __forceinline__ void x_load(uint4 (&xv)[M][XL], const XRows<M>& xr, int K) {
-  const int xq = K >> 3;
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
-      xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m])[i];
-    }
-}
-
-template <int M, int XL>
-__device__ __forceinline__ void x_store(const uint4 (&xv)[M][XL], int K, float4* xs) {
-  const int xq = K >> 3;
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      // piece i covers k = 8i .. 8i+7: chunk i/4, pieces 2(i%4) and 2(i%4)+1
-      const int i = min((int)threadIdx.x + j * kThreads, xq - 1);
-      const uint4 v = xv[m][j];
-      float4* d = xs + (i >> 2) * kXChunk<M> + m * 8 + 2 * (i & 3);
-      d[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-      d[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
-    }
 }
 
 // Rows handled by a block and the first row of this thread's row group.

@@ -275,94 +275,6 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
   }
 }
 
-// Persistent streaming kernel for one matrix with KSPLIT 1 (one row group per
-// row): K is a multiple of CPL * 512, the whole of x is staged once per block,
-// and each wave walks the row sets gw, gw + GW, ... (GW = waves in the grid),
-// each in K/(CPL*512) tiles, two items in flight.
-template <int M, int R, int CPL, int XL>
-__global__ __launch_bounds__(kThreads) void qmm_stream_kernel(const uint16_t* __restrict__ x, const RowSrc src,
-                                                              void* __restrict__ y, int out_f32) {
-  extern __shared__ float4 xs[];
-  constexpr int kSet = kSlots * R;   // rows per wave item
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t = lane & (kRowLanes - 1);
-  const int slot = lane / kRowLanes;
-  const int K = src.K;
-  const uint32_t wpr = (uint32_t)(K >> 3), gpr = (uint32_t)(K >> 6);
-  const int T = K / (CPL * 512);
-  const int nsets = (src.N + kSet - 1) / kSet;
-  const int GW = (int)gridDim.x * kWaves;
-  const int gw = (int)blockIdx.x * kWaves + wave;
-  const int nitems = (gw < nsets ? (nsets - 1 - gw) / GW + 1 : 0) * T;
-
-  XRows<M> xr;
-  size_t yoff[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    xr.p[m] = x + (size_t)m * K;
-    yoff[m] = (size_t)m * src.N;
-  }
-  uint4 xv[M][XL];
-  x_load<M, XL>(xv, xr, K);
-
-  LaneOff<R> lo;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint32_t lr = (uint32_t)(slot * R + r);
-    lo.q[r] = lr * wpr * 4u + (uint32_t)t * 16u;
-    lo.g[r] = lr * gpr * 2u + (uint32_t)(t >> 1) * 2u;
-  }
-
-  int iss_set = gw, iss_kt = 0, issued = 0;   // next item to issue
-  auto next_src = [&]() {
-    const ItemSrc is = item_src(src, iss_set * kSet, iss_kt, CPL * kRowLanes, kSet, issued < nitems, wpr, gpr);
-    ++issued;
-    if (++iss_kt == T) {
-      iss_kt = 0;
-      iss_set += GW;
-    }
-    return is;
-  };
-  Tile<CPL, R> A, B;
-  item_issue<CPL, R>(A, next_src(), lo);
-  item_issue<CPL, R>(B, next_src(), lo);
-  x_store<M, XL>(xv, K, xs);
-  __syncthreads();
-
-  float acc[R][M];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-  int c_set = gw, c_kt = 0;   // item being consumed
-  const float4* xlane = xs + t * kXChunk<M>;
-  auto finish = [&]() {
-    if (++c_kt == T) {
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = row16_sum(acc[r][m]);
-      store_to<M, R, 1>(acc, c_set * kSet + slot * R, src.N, y, yoff, out_f32 != 0);
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-      c_kt = 0;
-      c_set += GW;
-    }
-  };
-  for (int u = 0; u < nitems; u += 2) {
-    item_consume<M, R, CPL>(acc, A, xlane + c_kt * CPL * kRowLanes * kXChunk<M>);
-    finish();
-    item_issue<CPL, R>(A, next_src(), lo);
-    if (u + 1 >= nitems) break;
-    item_consume<M, R, CPL>(acc, B, xlane + c_kt * CPL * kRowLanes * kXChunk<M>);
-    finish();
-    item_issue<CPL, R>(B, next_src(), lo);
-  }
-}
-
 // Final argmax over the per-block keys of one activation row (blockIdx.x).
 // Every thread keeps eight independent loads in flight per round, so the
 // reduction costs one or two memory round trips rather than one per key; the
@@ -583,27 +495,6 @@ hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint1
   ml.m[0] = MatDesc{qw, s, b, y, N};
   ml.count = 1;
   return launch_dense_list<M, R, CPL, KSPLIT, PRE, DEPTH>(x, ml, out_f32, K, st);
-}
-
-template <int M>
-size_t stream_lds_bytes(int K) { return (size_t)(K / 32) * kXChunk<M> * sizeof(float4); }
-
-template <int M, int R, int CPL, int XL>
-hipError_t launch_stream(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
-                         int out_f32, int N, int K, int grid, hipStream_t st) {
-  const size_t lds = stream_lds_bytes<M>(K);
-  if (lds > 65536) {
-    static bool raised = false;   // the attribute is per function; setting it twice is harmless
-    if (!raised) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_stream_kernel<M, R, CPL, XL>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
-  }
-  const RowSrc src{qw, s, b, N, K};
-  hipLaunchKernelGGL((qmm_stream_kernel<M, R, CPL, XL>), dim3(grid), dim3(kThreads), lds, st, x, src, y, out_f32);
-  return hipGetLastError();
 }
 
 template <int M, int KSPLIT, int CLS>

@@ -57,10 +57,10 @@ def launch_grid(kernel: str, Ns) -> int:
     """Work-items launched by the dense kernel named `kernel` for matrices of
     Ns rows sharing one launch: a grid of (blocks of the tallest matrix) x
     (matrices) blocks; a block is 4 waves holding 16 row groups of R rows, or,
-    with a K-split of S, S waves sharing 4 row groups of R rows."""
-    M, R, CPL, KS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(",")[:4])
-    rows = (16 if KS == 1 else 4) * R
-    threads = 64 * (4 if KS == 1 else KS)
+    with a K-split of S, RS row sets of S waves sharing 4 row groups of R rows."""
+    M, R, CPL, KS, PRE, DEPTH, RS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(","))
+    rows = (16 if KS == 1 else 4 * RS) * R
+    threads = 64 * (4 if KS == 1 else KS * RS)
     return -(-max(Ns) // rows) * len(Ns) * threads
 
 

@@ -34,11 +34,12 @@ constexpr int kRowLanes = 16;
 constexpr int kSlots = kWave / kRowLanes;      // row groups per wave
 
 // Block shape for a K-split of S (KSPLIT): without a split, four waves hold
-// 16 rows; with one, each of S waves holds one S-th of the same four rows.
-template <int KSPLIT>
-constexpr int kBlockWaves = KSPLIT == 1 ? kWaves : KSPLIT;
-template <int KSPLIT>
-constexpr int kBlockThreads = kWave * kBlockWaves<KSPLIT>;
+// 16 rows; with one, each of S waves holds one S-th of the same four rows, and
+// a block may hold RS such row sets (S * RS waves sharing one activation tile).
+template <int KSPLIT, int RS = 1>
+constexpr int kBlockWaves = KSPLIT == 1 ? kWaves : KSPLIT * RS;
+template <int KSPLIT, int RS = 1>
+constexpr int kBlockThreads = kWave * kBlockWaves<KSPLIT, RS>;
 constexpr int kMaxM = 8;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -233,13 +234,13 @@ __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, f
 // fold into the load instructions' immediate fields); otherwise chunk slots
 // past the end of the tile load nothing (offset outside the resource) and are
 // skipped.
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS>
 __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
                                           int klen, float4* xs) {
   constexpr int LPR = kRowLanes * KSPLIT;
   constexpr int CS = CPL * LPR;                               // chunks per K-tile
   constexpr int KTILE = CS * 32;                              // codes per K-tile
-  constexpr int NT = kBlockThreads<KSPLIT>;
+  constexpr int NT = kBlockThreads<KSPLIT, RS>;
   constexpr int XL = (KTILE / 8 + NT - 1) / NT;                // 16-byte x loads per thread per row
   const int cseg = FULL ? CS : klen >> 5;    // chunks in this tile
   const int cbase = k0 >> 5;
@@ -444,10 +445,10 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 // chunks are consumed in order as they arrive.
 //
 // KSPLIT == 1: on return every lane of the row group holds the sums.
-// KSPLIT == S > 1: the S waves of the block share the rows; on return every
-//              lane of every wave holds the sums (combined in wave order).
+// KSPLIT == S > 1: the S waves of a row set share its rows; on return every
+//              lane of those waves holds the sums (combined in wave order).
 // xs must hold kXsF4<M, CPL, KSPLIT> float4.  Call with all threads (barriers).
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS = 1>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -460,11 +461,12 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   WaveRows w;
   w.wpr = (uint32_t)(K >> 3);
   w.gpr = (uint32_t)(K >> 6);
-  w.L = KSPLIT == 1 ? t : wave * kRowLanes + t;
+  w.L = KSPLIT == 1 ? t : (RS == 1 ? wave : wave % KSPLIT) * kRowLanes + t;
   w.slot = slot;
 
-  // Rows of this wave: [wave_row0, wave_row0 + kSlots*R).
-  const int wave_row0 = block_row0 + (KSPLIT == 1 ? wave * kSlots * R : 0);
+  // Rows of this wave: [wave_row0, wave_row0 + kSlots*R) (with a K-split,
+  // waves w .. w + KSPLIT - 1 of row set w / KSPLIT share them).
+  const int wave_row0 = block_row0 + (KSPLIT == 1 ? wave : RS == 1 ? 0 : wave / KSPLIT) * kSlots * R;
   const int nrows = max(0, min(kSlots * R, src.N - wave_row0));
   w.rq = make_rsrc(src.qw + (size_t)wave_row0 * w.wpr, (uint32_t)nrows * w.wpr * 4u);
   w.rs = make_rsrc(src.scales + (size_t)wave_row0 * w.gpr, (uint32_t)nrows * w.gpr * 2u);
@@ -486,9 +488,9 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   for (int k0 = kr; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
     if (klen == KTILE)
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true, RS>(acc, xr, w, k0, klen, xs);
     else
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false, RS>(acc, xr, w, k0, klen, xs);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -507,23 +509,24 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float v = red[((0 * kSlots + slot) * R + r) * M + m];
+        const int w0 = RS == 1 ? 0 : wave - wave % KSPLIT;   // first wave of this row set
+        float v = red[((w0 * kSlots + slot) * R + r) * M + m];
 #pragma unroll
-        for (int w2 = 1; w2 < KSPLIT; ++w2) v += red[((w2 * kSlots + slot) * R + r) * M + m];
+        for (int w2 = 1; w2 < KSPLIT; ++w2) v += red[(((w0 + w2) * kSlots + slot) * R + r) * M + m];
         acc[r][m] = v;
       }
   }
 }
 
 // Rows handled by a block and the first row of this thread's row group.
-template <int R, int KSPLIT>
+template <int R, int KSPLIT, int RS = 1>
 struct RowMap {
-  static constexpr int kRowsPerBlock = (KSPLIT == 1 ? kWaves * kSlots : kSlots) * R;
+  static constexpr int kRowsPerBlock = (KSPLIT == 1 ? kWaves : RS) * kSlots * R;
   __device__ static int first_row(int block_row0) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int slot = lane / kRowLanes;
-    const int group = KSPLIT == 1 ? wave * kSlots + slot : slot;
+    const int group = (KSPLIT == 1 ? wave : RS == 1 ? 0 : wave / KSPLIT) * kSlots + slot;
     return block_row0 + group * R;
   }
 };

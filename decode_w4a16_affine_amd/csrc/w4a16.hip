@@ -41,7 +41,12 @@ int ksplit_for(int N, int K) {
 // cover K exactly use straight-line loads with immediate offsets.  For M >= 6
 // the activation tile of a 5-chunk K-tile alone (M * 10 KiB per block) would
 // cap the CU at two blocks, so those rows take 2-chunk tiles.
-// KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile.
+// KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile;
+// from M = 2 a block holds two row sets (eight waves, eight row groups) that
+// share one staged activation tile, which halves the activation traffic per
+// row (down projection 2560<-10240: M = 2 9.9 -> 9.4 us, M = 3 12.3 -> 11.1 us,
+// M = 5 17.3 -> 16.2 us; at M = 1 one row set is faster, 6.5 vs 6.9 us).
+// RS: row sets per block (K-split only).
 // KSPLIT 5: one chunk per lane; two rows per lane from M = 2 (in the grouped
 // q/k/v launch, one row per lane doubles the blocks and cost 1.2-2 us per
 // launch at M = 2..5).
@@ -63,6 +68,7 @@ struct Sched<M, 1, CLS> {
                              : 2;
   static constexpr int PRE = 1;
   static constexpr int DEPTH = (R == 2 && M == 1) ? 3 : 2;
+  static constexpr int RS = 1;
 };
 template <int M, int CLS>
 struct Sched<M, 4, CLS> {
@@ -70,6 +76,7 @@ struct Sched<M, 4, CLS> {
   static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 ? 2 : 1);
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 2;
+  static constexpr int RS = (CLS == 1 && M >= 2) ? 2 : 1;
 };
 template <int M, int CLS>
 struct Sched<M, 5, CLS> {
@@ -77,6 +84,7 @@ struct Sched<M, 5, CLS> {
   static constexpr int CPL = 1;
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 1;
+  static constexpr int RS = 1;
 };
 
 // The routed product streams one expert's rows per distinct expert in the ids,
@@ -85,13 +93,22 @@ struct Sched<M, 5, CLS> {
 // 74.5 us, M = 1 13.2 -> 12.8 us).  Passes of at most two activation rows
 // (most experts serve one or two tokens; four-row passes cost occupancy).
 template <int MB, int KSPLIT, int CLS>
-struct RoutedSched : Sched<MB, KSPLIT, CLS> {};
+struct RoutedSched : Sched<MB, KSPLIT, CLS> {
+  static constexpr int RS = 1;
+};
 template <int MB, int CLS>
 struct RoutedSched<MB, 1, CLS> {
   static constexpr int R = 2;
   static constexpr int CPL = Sched<MB, 1, CLS | 4>::CPL;
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 2;
+  static constexpr int RS = 1;
+};
+// The LM head keeps one row set per block (its block maximum is taken over
+// the waves that hold finished sums).
+template <int M, int KSPLIT, int CLS>
+struct LmSched : Sched<M, KSPLIT, CLS> {
+  static constexpr int RS = 1;
 };
 constexpr int kRoutedPassRows = 2;
 
@@ -119,13 +136,10 @@ auto with_sched(int ksplit, int cls, F&& f) {
   }
 }
 
-template <int R, int KSPLIT>
-constexpr int rows_per_block_of() { return (KSPLIT == 1 ? kWaves * kSlots : kSlots) * R; }
-
 template <int M>
-int rows_per_block(int ksplit, int cls) {
+int lmhead_rows_per_block(int ksplit, int cls) {
   return with_sched(ksplit, cls, [](auto ks, auto c) {
-    return rows_per_block_of<Sched<M, decltype(ks)::value, decltype(c)::value>::R, decltype(ks)::value>();
+    return RowMap<LmSched<M, decltype(ks)::value, decltype(c)::value>::R, decltype(ks)::value>::kRowsPerBlock;
   });
 }
 
@@ -133,13 +147,13 @@ int rows_per_block(int ksplit, int cls) {
 // Kernels
 // ---------------------------------------------------------------------------
 
-template <int M, int R, int KSPLIT>
+template <int M, int R, int KSPLIT, int RS = 1>
 __device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first, int N, void* y,
                                          const size_t (&yoff)[M], bool out_f32) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int t = lane & (kRowLanes - 1);
-  if (KSPLIT > 1 && wave != 0) return;
+  if (KSPLIT > 1 && (RS == 1 ? wave : wave % KSPLIT) != 0) return;   // one wave per row set stores
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -183,13 +197,13 @@ struct MatArgs {
   int N[kMaxMats - 1];
 };
 
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
-__global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS>
+__global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
     const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
     int N0, int K, int out_f32, const MatArgs more) {
   __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
-  __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
-  using RM = RowMap<R, KSPLIT>;
+  __shared__ float red[kBlockWaves<KSPLIT, RS> * kSlots * R * M];
+  using RM = RowMap<R, KSPLIT, RS>;
   MatDesc d{qw0, scales0, biases0, y0, N0};
   if (blockIdx.y > 0) {
     const int mi = blockIdx.y - 1;
@@ -206,8 +220,8 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_dense_kernel(
   }
   const RowSrc src{d.qw, d.scales, d.biases, d.N, K};
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH>(acc, xr, src, block_row0, xs, red);
-  store_to<M, R, KSPLIT>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
+  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, RS>(acc, xr, src, block_row0, xs, red);
+  store_to<M, R, KSPLIT, RS>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
 }
 
 template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
@@ -466,9 +480,9 @@ w4a16_status_t check_weights(const uint16_t* x, const uint32_t* qw, const uint16
   return W4A16_OK;
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS>
 hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
-  using RM = RowMap<R, KSPLIT>;
+  using RM = RowMap<R, KSPLIT, RS>;
   long blocks = 0;
   MatArgs a{};
   for (int i = 0; i < ml.count; ++i) {
@@ -483,24 +497,24 @@ hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, 
   }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const MatDesc& m0 = ml.m[0];
-  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH>), dim3((unsigned)blocks, (unsigned)ml.count),
-                     dim3(kBlockThreads<KSPLIT>), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a);
+  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS>), dim3((unsigned)blocks, (unsigned)ml.count),
+                     dim3((kBlockThreads<KSPLIT, RS>)), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a);
   return hipGetLastError();
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE = CPL, int DEPTH = CPL>
+template <int M, int R, int CPL, int KSPLIT, int PRE = CPL, int DEPTH = CPL, int RS = 1>
 hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
                               int out_f32, int N, int K, hipStream_t st) {
   MatList ml{};
   ml.m[0] = MatDesc{qw, s, b, y, N};
   ml.count = 1;
-  return launch_dense_list<M, R, CPL, KSPLIT, PRE, DEPTH>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, R, CPL, KSPLIT, PRE, DEPTH, RS>(x, ml, out_f32, K, st);
 }
 
 template <int M, int KSPLIT, int CLS>
 hipError_t launch_dense(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   using S = Sched<M, KSPLIT, CLS>;
-  return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH, S::RS>(x, ml, out_f32, K, st);
 }
 
 // Every matrix of `ml` must have the K-split `ksplit`; the schedule class
@@ -531,7 +545,7 @@ hipError_t dense_dispatch(int M, int ksplit, const uint16_t* x, const MatList& m
 template <int M, int KSPLIT, int CLS>
 hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* logits,
                          int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
-  using S = Sched<M, KSPLIT, CLS>;
+  using S = LmSched<M, KSPLIT, CLS>;
   using RM = RowMap<S::R, KSPLIT>;
   const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   *nblocks = blocks;
@@ -582,26 +596,27 @@ int lmhead_blocks(int M, int N, int K) {
   const int cls = sched_class(N, K, ks);
   int rpb = 0;
   switch (M) {
-    case 1: rpb = rows_per_block<1>(ks, cls); break;
-    case 2: rpb = rows_per_block<2>(ks, cls); break;
-    case 3: rpb = rows_per_block<3>(ks, cls); break;
-    case 4: rpb = rows_per_block<4>(ks, cls); break;
-    case 5: rpb = rows_per_block<5>(ks, cls); break;
-    case 6: rpb = rows_per_block<6>(ks, cls); break;
-    case 7: rpb = rows_per_block<7>(ks, cls); break;
-    default: rpb = rows_per_block<8>(ks, cls); break;
+    case 1: rpb = lmhead_rows_per_block<1>(ks, cls); break;
+    case 2: rpb = lmhead_rows_per_block<2>(ks, cls); break;
+    case 3: rpb = lmhead_rows_per_block<3>(ks, cls); break;
+    case 4: rpb = lmhead_rows_per_block<4>(ks, cls); break;
+    case 5: rpb = lmhead_rows_per_block<5>(ks, cls); break;
+    case 6: rpb = lmhead_rows_per_block<6>(ks, cls); break;
+    case 7: rpb = lmhead_rows_per_block<7>(ks, cls); break;
+    default: rpb = lmhead_rows_per_block<8>(ks, cls); break;
   }
   return (N + rpb - 1) / rpb;
 }
 
 template <int M>
-void sched_of(int ks, int cls, int* R, int* CPL, int* PRE, int* DEPTH) {
+void sched_of(int ks, int cls, int* R, int* CPL, int* PRE, int* DEPTH, int* RS) {
   with_sched(ks, cls, [&](auto k, auto c) {
     using S = Sched<M, decltype(k)::value, decltype(c)::value>;
     *PRE = S::PRE;
     *DEPTH = S::DEPTH;
     *R = S::R;
     *CPL = S::CPL;
+    *RS = S::RS;
     return 0;
   });
 }
@@ -616,18 +631,18 @@ const char* w4a16_schedule_name(int M, int N, int K, int group) {
   static thread_local char buf[96];
   if (check_shape(M, N, K, group, W4A16_OUT_BF16) != W4A16_OK || M == 0 || N == 0) return "";
   const int ks = ksplit_for(N, K), cls = sched_class(N, K, ks);
-  int R = 0, CPL = 0, PRE = 0, DEPTH = 0;
+  int R = 0, CPL = 0, PRE = 0, DEPTH = 0, RS = 0;
   switch (M) {
-    case 1: sched_of<1>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
-    case 2: sched_of<2>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
-    case 3: sched_of<3>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
-    case 4: sched_of<4>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
-    case 5: sched_of<5>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
-    case 6: sched_of<6>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
-    case 7: sched_of<7>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
-    default: sched_of<8>(ks, cls, &R, &CPL, &PRE, &DEPTH); break;
+    case 1: sched_of<1>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
+    case 2: sched_of<2>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
+    case 3: sched_of<3>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
+    case 4: sched_of<4>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
+    case 5: sched_of<5>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
+    case 6: sched_of<6>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
+    case 7: sched_of<7>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
+    default: sched_of<8>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
   }
-  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d, %d, %d>", M, R, CPL, ks, PRE, DEPTH);
+  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d, %d, %d, %d>", M, R, CPL, ks, PRE, DEPTH, RS);
   return buf;
 }
 

@@ -174,10 +174,10 @@ const char *w4a16_status_str(w4a16_status_t s);
 
 /*
  * Name of the kernel instantiation w4a16_matmul launches for this shape, as
- * profilers report it ("qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH>":
+ * profilers report it ("qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS>":
  * activation rows, rows per lane, 16-byte chunks per lane per K-tile, waves
  * sharing a row, chunk slots whose loads are issued before the activations are
- * staged, chunk slots in flight per lane).
+ * staged, chunk slots in flight per lane, row sets per block when KSPLIT > 1).
  * "" when the arguments are invalid.  The string lives in thread-local storage
  * and stays valid until the next call on the same thread.
  */

@@ -133,9 +133,10 @@ def test_decode_projections_and_verify_batches(orc, name):
 # (4200, 4672) and (4500, 7680): one row group per row, walked in several
 # K-tiles (two full tiles and a ragged tail; three full tiles: the
 # double-buffered walk); (16400, 576) and (16390, 2560): N >= 16384, where the
-# rows per lane and the tile length change with M
+# rows per lane and the tile length change with M; (1003, 6208): a K-split row
+# whose blocks hold two row sets from M = 2, with a ragged last block
 RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560), (61, 2560), (300, 5120),
-          (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560)]
+          (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560), (1003, 6208)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)

@@ -7,11 +7,13 @@
 //   * A 16-byte load holds 32 consecutive codes of one row: half of a 64-code
 //     quantization group, so a load never straddles two groups.
 //   * 16 consecutive lanes ("a row group") stream one row: lane L reads the
-//     16-byte chunks c = L, L + LPR, L + 2*LPR, ... of the row, where LPR is 16
-//     (one row group per row) or 64 (the four waves of a block share a row:
-//     K-split for narrow matrices).  A wave holds four row groups.
+//     16-byte chunks c = L, L + LPR, L + 2*LPR, ... of the row, where LPR is
+//     16 * S: S = 1 (one row group per row) or S = 4 or 5 waves of a block
+//     sharing a row (K-split, for matrices of at most 4096 rows).  A wave holds
+//     four row groups; a K-split block may hold several such row sets.
 //   * Each lane streams R rows at once so one activation fetch from LDS serves
-//     R rows.  Activations are staged once per block into LDS as fp32.
+//     R rows.  Activations are staged per K-tile into LDS as fp32 (into two
+//     alternating buffers when a row spans several tiles).
 //   * Dequantization is literal: w = fma(s, q, b) in fp32 for every weight, with
 //     the code fed to v_fma_mix_f32 as an fp16 subnormal (bits q = value
 //     q * 2^-24, or 16q * 2^-24 for the odd nibble of a byte) and the scale
@@ -233,7 +235,9 @@ __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, f
 // range and all offsets are compile-time steps from one base per row (they
 // fold into the load instructions' immediate fields); otherwise chunk slots
 // past the end of the tile load nothing (offset outside the resource) and are
-// skipped.
+// skipped.  The staging and chunk body are those of x_stage_tile and
+// consume_slot written out in place (through the helpers the compiler
+// allocated 44-71% more registers for the K-split kernels).
 template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS>
 __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
                                           int klen, float4* xs) {

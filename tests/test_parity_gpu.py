@@ -235,12 +235,15 @@ def test_closed_forms_on_gpu(orc):
         full_check(orc, w, x, y64, absy, f"codes={c}")
 
 
+@pytest.mark.parametrize("K", [2560, 6208])
 @pytest.mark.parametrize("M", [1, 3, 8])
-def test_grouped_equals_separate_calls(orc, M):
+def test_grouped_equals_separate_calls(orc, M, K):
     # the q, k, v projections of a decode layer in one grouped call, plus a wide
-    # matrix in another K-split class and an empty one
-    shapes = [("q", 2560), ("k", 512), ("v", 512), ("wide", 5000), ("empty", 0)]
-    K = 2560
+    # matrix in another K-split class and an empty one; K = 6208 puts the narrow
+    # ones in the long-row K-split class (two row sets per block from M = 2),
+    # with row counts that leave partial blocks
+    shapes = ([("q", 2560), ("k", 512), ("v", 512), ("wide", 5000), ("empty", 0)] if K == 2560 else
+              [("q", 2568), ("k", 300), ("v", 13), ("wide", 4100), ("empty", 0)])
     x = synthetic.activations(M, K, seed=51)
     xd = dev_bf16(x)
     mats, outs, ws = [], [], []
@@ -251,7 +254,7 @@ def test_grouped_equals_separate_calls(orc, M):
         mats.append((dw.qw[:N], dw.s[:N], dw.b[:N], y))
         outs.append(y)
         ws.append((w, dw))
-    say(f"grouped q/k/v/wide/empty M={M}")
+    say(f"grouped q/k/v/wide/empty M={M} K={K}")
     w4.w4a16_matmul_grouped(xd, mats)
     torch.cuda.synchronize()
     for (name, N), y, (w, dw) in zip(shapes, outs, ws):
@@ -261,7 +264,7 @@ def test_grouped_equals_separate_calls(orc, M):
         assert np.array_equal(host_f32(y).view(np.uint32), ref.view(np.uint32)), name
         rows = np.arange(0, N, 7, dtype=np.int32)
         y64, absy = orc.qmm(x, w.qw, w.scales, w.biases, rows=rows)
-        check_f32(host_f32(y)[:, rows], y64, absy, f"grouped {name} M={M}")
+        check_f32(host_f32(y)[:, rows], y64, absy, f"grouped {name} M={M} K={K}")
 
 
 def test_deterministic_and_no_stray_writes(orc):

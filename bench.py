@@ -234,8 +234,18 @@ def config_timings(torch, w4, reps: int = 5):
         calls = [lambda c=c: w4.w4a16_lmhead_argmax(x, qw[c], sc[c], bi[c], logits, am, ws)
                  for c in (0, 1, 2, 0, 1, 2)]
         out["lm_head"][str(M)] = timed(calls, call_bytes(M, N, K) + 4 * M)
-    del qw, sc, bi
     log(f"lm_head: {out['lm_head']}")
+
+    # quantized row gather from the same (tied embedding) table to bf16: a
+    # decode step's tokens and a prefill-sized batch of seeded random rows
+    out["gather"] = {}
+    for R in (8, 4096):
+        rows = torch.from_numpy(np.random.default_rng(R).integers(0, N, size=R).astype(np.int32)).cuda()
+        emb = torch.empty((R, K), dtype=torch.bfloat16, device="cuda")
+        calls = [lambda c=c: w4.w4a16_gather_rows(qw[c], sc[c], bi[c], rows, emb) for c in (0, 1, 2, 0, 1, 2)]
+        out["gather"][str(R)] = timed(calls, R * (K // 2 + (K // 64) * 4 + 2 * K + 4))
+    del qw, sc, bi
+    log(f"gather: {out['gather']}")
 
     # square qmv / qmm
     t = synthetic.SQUARE
@@ -311,7 +321,7 @@ def main():
                     help="untimed replay time before each measurement (default: 1 s before the first, "
                          "0.25 s before the others; profiler runs use 0)")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the per-call timings of the tiny, LM-head, square and routed configurations")
+                    help="skip the per-call timings of the tiny, LM-head, row-gather, square and routed configurations")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy (a known-size reference for "

@@ -30,7 +30,7 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_
           5: "ERR_WORKSPACE", 6: "ERR_HIP"}
 
 EXPORTS = ("w4a16_matmul", "w4a16_matmul_grouped", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
-           "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_pack", "w4a16_status_str",
+           "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_gather_rows", "w4a16_pack", "w4a16_status_str",
            "w4a16_abi_version", "w4a16_schedule_name")
 
 
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                           _int, _int, _vp]
         L.w4a16_dequant.restype = _int
         L.w4a16_dequant.argtypes = [_vp, _vp, _vp, _vp, _int, _vp, _int, _int, _int, _vp]
+        L.w4a16_gather_rows.restype = _int
+        L.w4a16_gather_rows.argtypes = [_vp, _vp, _vp, _vp, _int, _vp, _int, _int, _int, _vp]
         L.w4a16_pack.restype = _int
         L.w4a16_pack.argtypes = [_vp, _vp, _int, _int, _vp]
         L.w4a16_status_str.restype = ctypes.c_char_p
@@ -192,6 +194,15 @@ def w4a16_dequant(qw, scales, biases, out, rows=None, group: int = GROUP, stream
                                _stream(stream)), "w4a16_dequant")
 
 
+def w4a16_gather_rows(qw, scales, biases, rows, out, group: int = GROUP, stream=None) -> None:
+    """out[R,K] (bf16) = rows[R] of the packed table, dequantized and rounded to bf16."""
+    _dtype(qw, torch.int32, "qw"); _dtype(rows, torch.int32, "rows"); _dtype(out, torch.bfloat16, "out")
+    N = qw.shape[0]
+    K = qw.shape[1] * 8
+    _check(lib().w4a16_gather_rows(_ptr(qw), _ptr(scales), _ptr(biases), _ptr(rows), rows.numel(), _ptr(out), N, K,
+                                   group, _stream(stream)), "w4a16_gather_rows")
+
+
 def w4a16_pack(codes, qw, stream=None) -> None:
     """codes uint8 [N,K] -> qw int32 [N,K/8] (first code in the lowest nibble)."""
     _dtype(codes, torch.uint8, "codes"); _dtype(qw, torch.int32, "qw")
@@ -240,6 +251,12 @@ def dequant(qw, scales, biases, rows=None, stream=None):
     R = rows.numel() if rows is not None else qw.shape[0]
     out = torch.empty((R, qw.shape[1] * 8), dtype=torch.float32, device=qw.device)
     w4a16_dequant(qw, scales, biases, out, rows=rows, stream=stream)
+    return out
+
+
+def gather_rows(qw, scales, biases, rows, stream=None):
+    out = torch.empty((rows.numel(), qw.shape[1] * 8), dtype=torch.bfloat16, device=qw.device)
+    w4a16_gather_rows(qw, scales, biases, rows, out, stream=stream)
     return out
 
 

@@ -443,6 +443,38 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(const uint32_t* __res
   }
 }
 
+// One packed word (8 codes) of a gathered row per thread and iteration: 8
+// literal fma dequantizations rounded to bf16, one 16-byte store, so a wave's
+// loads and stores each cover one contiguous range.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t* __restrict__ qw,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ biases,
+                                                          const int32_t* __restrict__ rows, int R,
+                                                          uint16_t* __restrict__ out, int N, int K) {
+  const size_t wpr = (size_t)(K >> 3);          // words per row
+  const size_t gpr = (size_t)(K >> 6);
+  const size_t total = (size_t)R * wpr;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / wpr;
+    const size_t j = i - r * wpr;
+    const int n = rows[r];
+    uint4 o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    if (n >= 0 && n < N) {
+      const uint32_t w = qw[(size_t)n * wpr + j];
+      const float s = __uint_as_float((uint32_t)scales[(size_t)n * gpr + (j >> 3)] << 16);
+      const float b = __uint_as_float((uint32_t)biases[(size_t)n * gpr + (j >> 3)] << 16);
+      float d[8];
+      if (needs_plain(s))
+        dequant8_plain(w, s, b, d);
+      else
+        dequant8_fast(w, s * 0x1p24f, s * 0x1p20f, b, d);
+      o = make_uint4(f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16), f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16),
+                     f32_to_bf16(d[4]) | (f32_to_bf16(d[5]) << 16), f32_to_bf16(d[6]) | (f32_to_bf16(d[7]) << 16));
+    }
+    reinterpret_cast<uint4*>(out + r * (size_t)K)[j] = o;
+  }
+}
+
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, uint32_t* __restrict__ qw,
                                                    size_t words) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x) {
@@ -785,6 +817,22 @@ w4a16_status_t w4a16_dequant(const uint32_t* qw, const uint16_t* scales, const u
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, qw, scales,
                      biases, rows, nrows, out, N, K);
+  return launched(hipGetLastError());
+}
+
+w4a16_status_t w4a16_gather_rows(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
+                                 const int32_t* rows, int R, uint16_t* out, int N, int K, int group, void* stream) {
+  if (group != 64) return W4A16_ERR_UNSUPPORTED;
+  if (N < 0 || R < 0 || K < 64 || K % 64 != 0) return W4A16_ERR_SHAPE;
+  if (R == 0) return W4A16_OK;
+  if (!qw || !scales || !biases || !rows || !out) return W4A16_ERR_NULL;
+  if (!aligned(qw, 4) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(rows, 4) || !aligned(out, 16))
+    return W4A16_ERR_ALIGN;
+  const size_t words = (size_t)R * (size_t)(K / 8);
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, qw, scales, biases,
+                     rows, R, out, N, K);
   return launched(hipGetLastError());
 }
 

@@ -164,6 +164,21 @@ w4a16_status_t w4a16_dequant(const uint32_t *qw, const uint16_t *scales, const u
                              void *stream);
 
 /*
+ * Quantized row gather for an embedding lookup: out[r][k] = bf16 round to
+ * nearest even of fma(s, q, b), i.e. of w4a16_dequant's value, for the table
+ * row n = rows[r] (tiny-llm page, Task 1: the selected rows are dequantized
+ * straight from the packed table, which is never expanded; the Gemma-4
+ * megakernel page dequantizes its 4-bit embedding inside the kernel).
+ * rows: int32 [R] on the device, any order, repeats allowed; a row index
+ * outside [0, N) writes bf16 NaN (0x7FC0) to that output row.
+ * qw: 4-byte aligned; out: bf16 [R][K], 16-byte aligned.  R == 0 succeeds
+ * without launching.
+ */
+w4a16_status_t w4a16_gather_rows(const uint32_t *qw, const uint16_t *scales, const uint16_t *biases,
+                                 const int32_t *rows, int R, uint16_t *out, int N, int K, int group,
+                                 void *stream);
+
+/*
  * Packed-weight loader: codes uint8 [N][K] (low 4 bits used) -> qw uint32
  * [N][K/8] in the layout above ("Packed Storage Layout").  K % 8 == 0.
  */

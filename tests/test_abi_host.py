@@ -142,7 +142,7 @@ def test_lmhead_workspace_rules(L):
     assert lm(group=256) == EUNSUP
 
 
-def test_dequant_and_pack_reject_bad_arguments(L):
+def test_dequant_gather_and_pack_reject_bad_arguments(L):
     dq = L.w4a16_dequant
     assert dq(A16, A16, A16, None, 0, A16, 16, 128, 32, None) == EUNSUP
     assert dq(A16, A16, A16, None, 0, A16, 16, 100, 64, None) == ESHAPE
@@ -150,6 +150,14 @@ def test_dequant_and_pack_reject_bad_arguments(L):
     assert dq(A16, A16, A16, None, 0, A16 + 4, 16, 128, 64, None) == EALIGN
     assert dq(None, A16, A16, None, 0, A16, 16, 128, 64, None) == ENULL
     assert dq(None, None, None, A16, 0, None, 16, 128, 64, None) == OK      # zero rows requested
+    gr = L.w4a16_gather_rows
+    assert gr(A16, A16, A16, A16, 4, A16, 16, 128, 32, None) == EUNSUP
+    assert gr(A16, A16, A16, A16, 4, A16, 16, 100, 64, None) == ESHAPE
+    assert gr(A16, A16, A16, A16, -1, A16, 16, 128, 64, None) == ESHAPE
+    assert gr(A4 + 2, A16, A16, A16, 4, A16, 16, 128, 64, None) == EALIGN
+    assert gr(A16, A16, A16, A16, 4, A16 + 4, 16, 128, 64, None) == EALIGN
+    assert gr(A16, A16, A16, None, 4, A16, 16, 128, 64, None) == ENULL
+    assert gr(None, None, None, None, 0, None, 16, 128, 64, None) == OK       # zero rows requested
     pk = L.w4a16_pack
     assert pk(A16, A16, 4, 12, None) == ESHAPE
     assert pk(None, A16, 4, 16, None) == ENULL

@@ -96,6 +96,28 @@ def test_dequant_bit_exact(orc):
     assert np.isnan(got[3]).all() and np.isnan(got[4]).all()
 
 
+def test_gather_rows_bit_exact(orc):
+    # embedding-style lookup: selected rows, repeats, any order, to bf16
+    for (N, K, kind) in [(300, 2560, "config"), (64, 2560, "crafted"), (9, 192, "crafted"), (5000, 64, "config")]:
+        say(f"gather rows N={N} K={K} {kind}")
+        w = synthetic.quantized_weights(N, K, seed=N + K + 1)
+        if kind == "crafted":
+            w.scales, w.biases = crafted_scales(N, K // 64, seed=N + 1)
+        rows = np.random.default_rng(N).integers(0, N, size=37).astype(np.int32)
+        rows[:3] = [N - 1, 0, N - 1]
+        got = host_bits(w4.gather_rows(dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases), dev_i32(rows)))
+        torch.cuda.synchronize()
+        ref = orc.f64_to_bf16(orc.dequant_rows(w.qw, w.scales, w.biases, K, rows=rows).astype(np.float64))
+        assert np.array_equal(got, ref), (N, K, kind)
+    say("gather rows: out-of-range rows give NaN rows, the others are untouched by them")
+    w = synthetic.quantized_weights(40, 320, seed=6)
+    rows = np.array([39, 40, -1, 0, 2147483647, 17], dtype=np.int32)
+    got = host_bits(w4.gather_rows(dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases), dev_i32(rows)))
+    ref = orc.f64_to_bf16(orc.dequant_rows(w.qw, w.scales, w.biases, 320, rows=[39, 0, 17]).astype(np.float64))
+    assert np.array_equal(got[[0, 3, 5]], ref)
+    assert (got[[1, 2, 4]] == 0x7FC0).all()
+
+
 # ---------------------------------------------------------------------------
 # Dense product: the five workloads and their edges
 # ---------------------------------------------------------------------------

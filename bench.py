@@ -41,9 +41,9 @@ FIRST_WARM_S = 1.0
 WARM_S = 0.25
 
 
-def call_bytes(M: int, N: int, K: int) -> int:
+def call_bytes(M: int, N: int, K: int, group: int = 64) -> int:
     """Algorithmic bytes of one product: codes + scales + biases + x + y (bf16)."""
-    return N * K // 2 + N * (K // 64) * 4 + 2 * M * K + 2 * M * N
+    return N * K // 2 + N * (K // group) * 4 + 2 * M * K + 2 * M * N
 
 
 def step_bytes(M: int, layers: int) -> int:
@@ -58,7 +58,7 @@ def launch_grid(kernel: str, Ns) -> int:
     Ns rows sharing one launch: a grid of (blocks of the tallest matrix) x
     (matrices) blocks; a block is 4 waves holding 16 row groups of R rows, or,
     with a K-split of S, RS row sets of S waves sharing 4 row groups of R rows."""
-    M, R, CPL, KS, PRE, DEPTH, RS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(","))
+    M, R, CPL, KS, PRE, DEPTH, RS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(",")[:7])
     rows = (16 if KS == 1 else 4 * RS) * R
     threads = 64 * (4 if KS == 1 else KS * RS)
     return -(-max(Ns) // rows) * len(Ns) * threads
@@ -247,6 +247,24 @@ def config_timings(torch, w4, reps: int = 5):
     del qw, sc, bi
     log(f"gather: {out['gather']}")
 
+    # group 128 (scales and biases per 128 codes): the largest decode
+    # projections and the square matrix at M = 1 and a verify batch
+    out["group128"] = {}
+    for name, (N, K) in (("gate_up", synthetic.PROJECTIONS["gate_up"]), ("down", synthetic.PROJECTIONS["down"]),
+                         ("square", (synthetic.SQUARE["N"], synthetic.SQUARE["K"]))):
+        w = synthetic.quantized_weights(N, K, group=128, seed=0, tag=(N, 128))
+        copies = max(3, -(-(512 << 20) // w.nbytes))   # one pass over the copies: > 2x the 256 MB cache
+        qw, sc, bi = upload(w, copies)
+        del w
+        out["group128"][name] = {}
+        for M in (1, 5):
+            x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(N, 128)).view(np.int16)).view(torch.bfloat16).cuda()
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            calls = [lambda c=c: w4.w4a16_matmul(x, qw[c], sc[c], bi[c], y, group=128) for c in range(copies)]
+            out["group128"][name][str(M)] = timed(calls, call_bytes(M, N, K, 128))
+        del qw, sc, bi
+    log(f"group128: {out['group128']}")
+
     # square qmv / qmm
     t = synthetic.SQUARE
     N, K = t["N"], t["K"]
@@ -321,7 +339,7 @@ def main():
                     help="untimed replay time before each measurement (default: 1 s before the first, "
                          "0.25 s before the others; profiler runs use 0)")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the per-call timings of the tiny, LM-head, row-gather, square and routed configurations")
+                    help="skip the per-call timings of the tiny, LM-head, row-gather, group-128, square and routed configurations")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy (a known-size reference for "

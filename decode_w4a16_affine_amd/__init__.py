@@ -224,39 +224,41 @@ def w4a16_schedule_name(M: int, N: int, K: int, group: int = GROUP) -> str:
 
 # ---- allocating conveniences (torch allocates; the library computes) ------------
 
-def matmul(x, qw, scales, biases, out_dtype=torch.bfloat16, stream=None):
+def matmul(x, qw, scales, biases, out_dtype=torch.bfloat16, group: int = GROUP, stream=None):
     y = torch.empty((x.shape[0], qw.shape[0]), dtype=out_dtype, device=x.device)
-    w4a16_matmul(x, qw, scales, biases, y, stream=stream)
+    w4a16_matmul(x, qw, scales, biases, y, group=group, stream=stream)
     return y
 
 
-def matmul_id(x, qw, scales, biases, ids, x_per_slot=False, out_dtype=torch.bfloat16, stream=None):
+def matmul_id(x, qw, scales, biases, ids, x_per_slot=False, out_dtype=torch.bfloat16, group: int = GROUP,
+              stream=None):
     y = torch.empty((ids.shape[0], ids.shape[1], qw.shape[1]), dtype=out_dtype, device=x.device)
-    w4a16_matmul_id(x, qw, scales, biases, ids, y, x_per_slot=x_per_slot, stream=stream)
+    w4a16_matmul_id(x, qw, scales, biases, ids, y, x_per_slot=x_per_slot, group=group, stream=stream)
     return y
 
 
-def lmhead_argmax(x, qw, scales, biases, want_logits=True, out_dtype=torch.bfloat16, stream=None):
+def lmhead_argmax(x, qw, scales, biases, want_logits=True, out_dtype=torch.bfloat16, group: int = GROUP,
+                  stream=None):
     M, K = x.shape
     N = qw.shape[0]
-    ws = torch.empty(max(1, w4a16_lmhead_argmax_workspace_bytes(M, N, K)), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(max(1, w4a16_lmhead_argmax_workspace_bytes(M, N, K, group)), dtype=torch.uint8, device=x.device)
     am = torch.empty(M, dtype=torch.int32, device=x.device)
     logits = torch.empty((M, N), dtype=out_dtype, device=x.device) if want_logits else None
-    w4a16_lmhead_argmax(x, qw, scales, biases, logits, am, ws, stream=stream,
+    w4a16_lmhead_argmax(x, qw, scales, biases, logits, am, ws, group=group, stream=stream,
                         out_dtype=OUT_F32 if out_dtype == torch.float32 else OUT_BF16)
     return am, logits
 
 
-def dequant(qw, scales, biases, rows=None, stream=None):
+def dequant(qw, scales, biases, rows=None, group: int = GROUP, stream=None):
     R = rows.numel() if rows is not None else qw.shape[0]
     out = torch.empty((R, qw.shape[1] * 8), dtype=torch.float32, device=qw.device)
-    w4a16_dequant(qw, scales, biases, out, rows=rows, stream=stream)
+    w4a16_dequant(qw, scales, biases, out, rows=rows, group=group, stream=stream)
     return out
 
 
-def gather_rows(qw, scales, biases, rows, stream=None):
+def gather_rows(qw, scales, biases, rows, group: int = GROUP, stream=None):
     out = torch.empty((rows.numel(), qw.shape[1] * 8), dtype=torch.bfloat16, device=qw.device)
-    w4a16_gather_rows(qw, scales, biases, rows, out, stream=stream)
+    w4a16_gather_rows(qw, scales, biases, rows, out, group=group, stream=stream)
     return out
 
 

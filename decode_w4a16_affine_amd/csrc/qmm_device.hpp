@@ -44,6 +44,12 @@ template <int KSPLIT, int RS = 1>
 constexpr int kBlockThreads = kWave * kBlockWaves<KSPLIT, RS>;
 constexpr int kMaxM = 8;
 
+// Quantization group G (64 or 128 codes): a 16-byte chunk holds 32 codes, so
+// a group spans G / 32 chunks and its scale (2 bytes) advances by 64 / G bytes
+// per chunk on average; a chunk never straddles two groups.
+template <int G>
+constexpr int kChunksPerGroup = G / 32;
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -238,7 +244,7 @@ __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, f
 // skipped.  The staging and chunk body are those of x_stage_tile and
 // consume_slot written out in place (through the helpers the compiler
 // allocated 44-71% more registers for the K-split kernels).
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS, int G>
 __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
                                           int klen, float4* xs) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -269,15 +275,16 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
   for (int r = 0; r < R; ++r) {
     const uint32_t lr = (uint32_t)(w.slot * R + r);
     qb[r] = lr * w.wpr * 4u + (uint32_t)(cbase + L) * 16u;   // byte offset of chunk slot 0
-    gb[r] = lr * w.gpr * 2u + (uint32_t)((cbase + L) >> 1) * 2u;
+    gb[r] = lr * w.gpr * 2u + (uint32_t)(cbase + L) / kChunksPerGroup<G> * 2u;
   }
   auto load_slot = [&](int j) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      // chunk c = L + j*LPR; LPR is even, so its group is ((cbase + L) >> 1) + j*LPR/2
+      // chunk c = cbase + L + j*LPR; LPR is a multiple of G/32, so its group is
+      // (cbase + L) / (G/32) + j*LPR/(G/32)
       const bool ok = FULL || L + j * LPR < cseg;
       const uint32_t oq = ok ? qb[r] + (uint32_t)(j * LPR * 16) : kOffNone;
-      const uint32_t og = ok ? gb[r] + (uint32_t)(j * LPR) : kOffNone;
+      const uint32_t og = ok ? gb[r] + (uint32_t)(j * LPR / kChunksPerGroup<G>) * 2u : kOffNone;
       tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, 0));
       tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
       tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
@@ -355,7 +362,7 @@ constexpr int kXsF4 = M * 8 * CPL * kRowLanes * KSPLIT * (kRolled<M, CPL, KSPLIT
 // vmcnt waits stay chunk-exact.  Every lane consumes the same chunks in the same
 // order with the same body as tile_pass: the sums are bitwise those of the
 // tile-by-tile walk.  xs must hold 2 * M * 8 * CPL * 16 float4.
-template <int M, int R, int CPL, int PRE, int DEPTH>
+template <int M, int R, int CPL, int PRE, int DEPTH, int G>
 __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w,
                                              int ntiles, float4* xs) {
   constexpr int LPR = kRowLanes;
@@ -387,7 +394,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
   for (int r = 0; r < R; ++r) {
     const uint32_t lr = (uint32_t)(w.slot * R + r);
     qb[r] = lr * w.wpr * 4u + (uint32_t)L * 16u;
-    gb[r] = lr * w.gpr * 2u + (uint32_t)(L >> 1) * 2u;
+    gb[r] = lr * w.gpr * 2u + (uint32_t)L / kChunksPerGroup<G> * 2u;
   }
   // slot j of the current tile (NEXT: of the following tile; none past the last)
   auto load = [&](int j, bool next, bool live) {
@@ -395,7 +402,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
     for (int r = 0; r < R; ++r) {
       const uint32_t step = (uint32_t)((next ? CS : 0) + j * LPR);
       const uint32_t oq = live ? qb[r] + step * 16u : kOffNone;
-      const uint32_t og = live ? gb[r] + step : kOffNone;
+      const uint32_t og = live ? gb[r] + step / kChunksPerGroup<G> * 2u : kOffNone;
       tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, 0));
       tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
       tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
@@ -428,7 +435,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       qb[r] += (uint32_t)CS * 16u;
-      gb[r] += (uint32_t)CS;
+      gb[r] += (uint32_t)(CS / kChunksPerGroup<G>) * 2u;
     }
     // tile t + 1's activations into the other buffer (last read during tile
     // t - 1, which every wave finished before the previous barrier)
@@ -452,7 +459,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 // KSPLIT == S > 1: the S waves of a row set share its rows; on return every
 //              lane of those waves holds the sums (combined in wave order).
 // xs must hold kXsF4<M, CPL, KSPLIT> float4.  Call with all threads (barriers).
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS = 1>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS = 1, int G = 64>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -464,7 +471,7 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   const int K = src.K;
   WaveRows w;
   w.wpr = (uint32_t)(K >> 3);
-  w.gpr = (uint32_t)(K >> 6);
+  w.gpr = (uint32_t)K / G;
   w.L = KSPLIT == 1 ? t : (RS == 1 ? wave : wave % KSPLIT) * kRowLanes + t;
   w.slot = slot;
 
@@ -485,16 +492,16 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   if constexpr (kRolled<M, CPL, KSPLIT>) {
     const int nfull = K / KTILE;
     if (nfull >= 2) {
-      rolled_tiles<M, R, CPL, PRE, DEPTH>(acc, xr, w, nfull, xs);
+      rolled_tiles<M, R, CPL, PRE, DEPTH, G>(acc, xr, w, nfull, xs);
       kr = nfull * KTILE;
     }
   }
   for (int k0 = kr; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
     if (klen == KTILE)
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true, RS>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true, RS, G>(acc, xr, w, k0, klen, xs);
     else
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false, RS>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false, RS, G>(acc, xr, w, k0, klen, xs);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)

@@ -197,7 +197,7 @@ struct MatArgs {
   int N[kMaxMats - 1];
 };
 
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS, int G>
 __global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
     const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
     int N0, int K, int out_f32, const MatArgs more) {
@@ -220,11 +220,11 @@ __global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
   }
   const RowSrc src{d.qw, d.scales, d.biases, d.N, K};
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, RS>(acc, xr, src, block_row0, xs, red);
+  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>(acc, xr, src, block_row0, xs, red);
   store_to<M, R, KSPLIT, RS>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int G>
 __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const uint16_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ scales,
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
   const int block_row0 = blockIdx.x * RM::kRowsPerBlock;
   const int row_first = RM::first_row(block_row0);
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH>(acc, xr, src, block_row0, xs, red);
+  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, 1, G>(acc, xr, src, block_row0, xs, red);
   if (logits) store_to<M, R, KSPLIT>(acc, row_first, N, logits, yoff, out_f32 != 0);
 
   // Block maximum of the (value, index) keys: every lane of a row group holds
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kFinalThreads) void argmax_finalize_kernel(const ui
 }
 
 // One pass of the routed product: C slots routed to one expert.
-template <int C, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
+template <int C, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int G>
 __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, int x_per_slot, int top_k,
                                             const RowSrc& src, int block_row0, void* y, bool out_f32, float4* xs,
                                             float* red) {
@@ -339,11 +339,11 @@ __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, 
     yoff[i] = (size_t)sl * src.N;
   }
   float acc[R][C];
-  block_rows<C, R, CPL, KSPLIT, PRE, DEPTH>(acc, xr, src, block_row0, xs, red);
+  block_rows<C, R, CPL, KSPLIT, PRE, DEPTH, 1, G>(acc, xr, src, block_row0, xs, red);
   store_to<C, R, KSPLIT>(acc, RM::first_row(block_row0), src.N, y, yoff, out_f32);
 }
 
-template <int MB, int R, int CPL, int KSPLIT, int PRE, int DEPTH>
+template <int MB, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int G>
 // (Arguments ordered so that what a block needs before its first memory access
 // sits in the 16 dwords the hardware preloads into scalar registers.)
 __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(
     if (__ballot(v == e)) return;
   }
   const size_t wpr = (size_t)(K >> 3);
-  const size_t gpr = (size_t)(K >> 6);
+  const size_t gpr = (size_t)((uint32_t)K / G);
   const RowSrc src{qw + (size_t)e * N * wpr, scales + (size_t)e * N * gpr, biases + (size_t)e * N * gpr, N, K};
   // The slots routed to e, ascending, in passes of at most MB activation rows;
   // each pass takes the lowest set bits of the current 64-slot ballot, so the
@@ -403,10 +403,10 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_routed_kernel(
         m &= m - 1;
       }
       switch (cnt) {
-        case 1: routed_pass<1, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-        case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-        case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
-        default: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT, PRE, DEPTH>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+        case 1: routed_pass<1, R, CPL, KSPLIT, PRE, DEPTH, G>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+        case 2: if constexpr (MB >= 2) routed_pass<2, R, CPL, KSPLIT, PRE, DEPTH, G>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+        case 3: if constexpr (MB >= 3) routed_pass<3, R, CPL, KSPLIT, PRE, DEPTH, G>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
+        default: if constexpr (MB >= 4) routed_pass<4, R, CPL, KSPLIT, PRE, DEPTH, G>(list, x, x_per_slot, top_k, src, block_row0, y, out_f32, xs, red); break;
       }
     }
   }
@@ -416,9 +416,9 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(const uint32_t* __res
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ biases,
                                                            const int32_t* __restrict__ rows, int R,
-                                                           float* __restrict__ out, int N, int K) {
+                                                           float* __restrict__ out, int N, int K, int wg_shift) {
   const size_t wpr = (size_t)(K >> 3);
-  const size_t gpr = (size_t)(K >> 6);
+  const size_t gpr = (size_t)(K >> 3 >> wg_shift);   // words per group: 1 << wg_shift
   const size_t total = (size_t)R * wpr;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const size_t r = i / wpr;
@@ -430,8 +430,8 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(const uint32_t* __res
       for (int q = 0; q < 8; ++q) o[q] = __builtin_nanf("");
     } else {
       const uint32_t w = qw[(size_t)n * wpr + j];
-      const float s = __uint_as_float((uint32_t)scales[(size_t)n * gpr + (j >> 3)] << 16);
-      const float b = __uint_as_float((uint32_t)biases[(size_t)n * gpr + (j >> 3)] << 16);
+      const float s = __uint_as_float((uint32_t)scales[(size_t)n * gpr + (j >> wg_shift)] << 16);
+      const float b = __uint_as_float((uint32_t)biases[(size_t)n * gpr + (j >> wg_shift)] << 16);
       if (needs_plain(s))
         dequant8_plain(w, s, b, o);
       else
@@ -450,9 +450,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t* __rest
                                                           const uint16_t* __restrict__ scales,
                                                           const uint16_t* __restrict__ biases,
                                                           const int32_t* __restrict__ rows, int R,
-                                                          uint16_t* __restrict__ out, int N, int K) {
+                                                          uint16_t* __restrict__ out, int N, int K, int wg_shift) {
   const size_t wpr = (size_t)(K >> 3);          // words per row
-  const size_t gpr = (size_t)(K >> 6);
+  const size_t gpr = (size_t)(K >> 3 >> wg_shift);   // words per group: 1 << wg_shift
   const size_t total = (size_t)R * wpr;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const size_t r = i / wpr;
@@ -461,8 +461,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t* __rest
     uint4 o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
     if (n >= 0 && n < N) {
       const uint32_t w = qw[(size_t)n * wpr + j];
-      const float s = __uint_as_float((uint32_t)scales[(size_t)n * gpr + (j >> 3)] << 16);
-      const float b = __uint_as_float((uint32_t)biases[(size_t)n * gpr + (j >> 3)] << 16);
+      const float s = __uint_as_float((uint32_t)scales[(size_t)n * gpr + (j >> wg_shift)] << 16);
+      const float b = __uint_as_float((uint32_t)biases[(size_t)n * gpr + (j >> wg_shift)] << 16);
       float d[8];
       if (needs_plain(s))
         dequant8_plain(w, s, b, d);
@@ -494,12 +494,14 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 w4a16_status_t launched(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+bool group_supported(int group) { return group == 64 || group == 128; }
+
 w4a16_status_t check_shape(int M, int N, int K, int group, int out_dtype) {
-  if (group != 64) return W4A16_ERR_UNSUPPORTED;
+  if (!group_supported(group)) return W4A16_ERR_UNSUPPORTED;
   if (out_dtype != W4A16_OUT_BF16 && out_dtype != W4A16_OUT_F32) return W4A16_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return W4A16_ERR_SHAPE;
   if (M > W4A16_MAX_M) return W4A16_ERR_UNSUPPORTED;
-  if (K < 64 || K % 64 != 0) return W4A16_ERR_SHAPE;
+  if (K < group || K % group != 0) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
 
@@ -512,7 +514,7 @@ w4a16_status_t check_weights(const uint16_t* x, const uint32_t* qw, const uint16
   return W4A16_OK;
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS, int G>
 hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   using RM = RowMap<R, KSPLIT, RS>;
   long blocks = 0;
@@ -529,75 +531,97 @@ hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, 
   }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const MatDesc& m0 = ml.m[0];
-  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS>), dim3((unsigned)blocks, (unsigned)ml.count),
+  hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>), dim3((unsigned)blocks, (unsigned)ml.count),
                      dim3((kBlockThreads<KSPLIT, RS>)), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a);
   return hipGetLastError();
 }
 
-template <int M, int R, int CPL, int KSPLIT, int PRE = CPL, int DEPTH = CPL, int RS = 1>
+template <int M, int R, int CPL, int KSPLIT, int PRE = CPL, int DEPTH = CPL, int RS = 1, int G = 64>
 hipError_t launch_dense_sched(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* y,
                               int out_f32, int N, int K, hipStream_t st) {
   MatList ml{};
   ml.m[0] = MatDesc{qw, s, b, y, N};
   ml.count = 1;
-  return launch_dense_list<M, R, CPL, KSPLIT, PRE, DEPTH, RS>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>(x, ml, out_f32, K, st);
 }
 
-template <int M, int KSPLIT, int CLS>
+template <int M, int KSPLIT, int CLS, int G>
 hipError_t launch_dense(const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   using S = Sched<M, KSPLIT, CLS>;
-  return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH, S::RS>(x, ml, out_f32, K, st);
+  return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH, S::RS, G>(x, ml, out_f32, K, st);
 }
 
 // Every matrix of `ml` must have the K-split `ksplit`; the schedule class
 // follows the tallest matrix (the class never changes a row's arithmetic).
-template <int M>
+template <int M, int G>
 hipError_t dense_by_split(int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K, hipStream_t st) {
   int nmax = 0;
   for (int i = 0; i < ml.count; ++i) nmax = ml.m[i].N > nmax ? ml.m[i].N : nmax;
   return with_sched(ksplit, sched_class(nmax, K, ksplit), [&](auto ks, auto c) {
-    return launch_dense<M, decltype(ks)::value, decltype(c)::value>(x, ml, out_f32, K, st);
+    return launch_dense<M, decltype(ks)::value, decltype(c)::value, G>(x, ml, out_f32, K, st);
   });
 }
 
-hipError_t dense_dispatch(int M, int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K,
-                          hipStream_t st) {
+template <int G>
+hipError_t dense_dispatch_g(int M, int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K,
+                            hipStream_t st) {
   switch (M) {
-    case 1: return dense_by_split<1>(ksplit, x, ml, out_f32, K, st);
-    case 2: return dense_by_split<2>(ksplit, x, ml, out_f32, K, st);
-    case 3: return dense_by_split<3>(ksplit, x, ml, out_f32, K, st);
-    case 4: return dense_by_split<4>(ksplit, x, ml, out_f32, K, st);
-    case 5: return dense_by_split<5>(ksplit, x, ml, out_f32, K, st);
-    case 6: return dense_by_split<6>(ksplit, x, ml, out_f32, K, st);
-    case 7: return dense_by_split<7>(ksplit, x, ml, out_f32, K, st);
-    default: return dense_by_split<8>(ksplit, x, ml, out_f32, K, st);
+    case 1: return dense_by_split<1, G>(ksplit, x, ml, out_f32, K, st);
+    case 2: return dense_by_split<2, G>(ksplit, x, ml, out_f32, K, st);
+    case 3: return dense_by_split<3, G>(ksplit, x, ml, out_f32, K, st);
+    case 4: return dense_by_split<4, G>(ksplit, x, ml, out_f32, K, st);
+    case 5: return dense_by_split<5, G>(ksplit, x, ml, out_f32, K, st);
+    case 6: return dense_by_split<6, G>(ksplit, x, ml, out_f32, K, st);
+    case 7: return dense_by_split<7, G>(ksplit, x, ml, out_f32, K, st);
+    default: return dense_by_split<8, G>(ksplit, x, ml, out_f32, K, st);
   }
 }
 
-template <int M, int KSPLIT, int CLS>
+hipError_t dense_dispatch(int M, int ksplit, const uint16_t* x, const MatList& ml, int out_f32, int K, int group,
+                          hipStream_t st) {
+  return group == 128 ? dense_dispatch_g<128>(M, ksplit, x, ml, out_f32, K, st)
+                      : dense_dispatch_g<64>(M, ksplit, x, ml, out_f32, K, st);
+}
+
+template <int M, int KSPLIT, int CLS, int G>
 hipError_t launch_lmhead(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* logits,
                          int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
   using S = LmSched<M, KSPLIT, CLS>;
   using RM = RowMap<S::R, KSPLIT>;
   const int blocks = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   *nblocks = blocks;
-  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH>), dim3(blocks), dim3(kBlockThreads<KSPLIT>), 0,
+  hipLaunchKernelGGL((qmm_lmhead_kernel<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH, G>), dim3(blocks), dim3(kBlockThreads<KSPLIT>), 0,
                      st, x, qw, s, b,
                      logits, out_f32, partial, N, K);
   return hipGetLastError();
 }
 
-template <int M>
+template <int M, int G>
 hipError_t lmhead_by_split(int ksplit, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                            void* logits, int out_f32, uint64_t* partial, int N, int K, hipStream_t st, int* nblocks) {
   return with_sched(ksplit, sched_class(N, K, ksplit), [&](auto ks, auto c) {
-    return launch_lmhead<M, decltype(ks)::value, decltype(c)::value>(x, qw, s, b, logits, out_f32, partial, N, K, st,
+    return launch_lmhead<M, decltype(ks)::value, decltype(c)::value, G>(x, qw, s, b, logits, out_f32, partial, N, K, st,
                                                                      nblocks);
   });
 }
 
 // Routed kernels: MB = most slots one expert is processed with per pass.
-template <int MB, int KSPLIT, int CLS>
+template <int G>
+hipError_t lmhead_dispatch(int M, int ks, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                           void* logits, int f32, uint64_t* partial, int N, int K, hipStream_t st, int* nb) {
+  switch (M) {
+    case 1: return lmhead_by_split<1, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+    case 2: return lmhead_by_split<2, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+    case 3: return lmhead_by_split<3, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+    case 4: return lmhead_by_split<4, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+    case 5: return lmhead_by_split<5, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+    case 6: return lmhead_by_split<6, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+    case 7: return lmhead_by_split<7, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+    default: return lmhead_by_split<8, G>(ks, x, qw, s, b, logits, f32, partial, N, K, st, nb);
+  }
+}
+
+template <int MB, int KSPLIT, int CLS, int G>
 hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                          const int32_t* ids, void* y, int out_f32, int M, int top_k, int E, int N, int K,
                          hipStream_t st) {
@@ -606,19 +630,19 @@ hipError_t launch_routed(const uint16_t* x, int x_per_slot, const uint32_t* qw, 
   const int tiles = (N + RM::kRowsPerBlock - 1) / RM::kRowsPerBlock;
   const size_t blocks = (size_t)tiles * M * top_k;
   if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((qmm_routed_kernel<MB, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH, G>), dim3((unsigned)blocks),
                      dim3(kBlockThreads<KSPLIT>), 0, st,
                      x, qw, s, b, ids, y, N, K, tiles, M, top_k, E, x_per_slot, out_f32);
   return hipGetLastError();
 }
 
-template <int MB>
+template <int MB, int G>
 hipError_t routed_by_split(int ksplit, const uint16_t* x, int x_per_slot, const uint32_t* qw, const uint16_t* s,
                            const uint16_t* b, const int32_t* ids, void* y, int out_f32, int M, int top_k, int E, int N,
                            int K, hipStream_t st) {
   // the class follows one expert's matrix (N rows), never the routed total
   return with_sched(ksplit, sched_class(N, K, ksplit), [&](auto ks, auto c) {
-    return launch_routed<MB, decltype(ks)::value, decltype(c)::value>(x, x_per_slot, qw, s, b, ids, y, out_f32, M,
+    return launch_routed<MB, decltype(ks)::value, decltype(c)::value, G>(x, x_per_slot, qw, s, b, ids, y, out_f32, M,
                                                                       top_k, E, N, K, st);
   });
 }
@@ -674,7 +698,7 @@ const char* w4a16_schedule_name(int M, int N, int K, int group) {
     case 7: sched_of<7>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
     default: sched_of<8>(ks, cls, &R, &CPL, &PRE, &DEPTH, &RS); break;
   }
-  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d, %d, %d, %d>", M, R, CPL, ks, PRE, DEPTH, RS);
+  snprintf(buf, sizeof buf, "qmm_dense_kernel<%d, %d, %d, %d, %d, %d, %d, %d>", M, R, CPL, ks, PRE, DEPTH, RS, group);
   return buf;
 }
 
@@ -682,8 +706,8 @@ const char* w4a16_status_str(w4a16_status_t s) {
   switch (s) {
     case W4A16_OK: return "ok";
     case W4A16_ERR_NULL: return "a required pointer is NULL";
-    case W4A16_ERR_SHAPE: return "invalid shape (K must be a positive multiple of 64; sizes non-negative)";
-    case W4A16_ERR_UNSUPPORTED: return "unsupported (group must be 64, M at most 8, out_dtype bf16 or f32)";
+    case W4A16_ERR_SHAPE: return "invalid shape (K must be a positive multiple of the group; sizes non-negative)";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported (group must be 64 or 128, M at most 8, out_dtype bf16 or f32)";
     case W4A16_ERR_ALIGN: return "pointer misaligned";
     case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
     case W4A16_ERR_HIP: return "HIP runtime rejected the launch";
@@ -701,7 +725,7 @@ w4a16_status_t w4a16_matmul(const uint16_t* x, const uint32_t* qw, const uint16_
   MatList ml{};
   ml.m[0] = MatDesc{qw, scales, biases, y, N};
   ml.count = 1;
-  return launched(dense_dispatch(M, ksplit_for(N, K), x, ml, out_dtype == W4A16_OUT_F32, K, (hipStream_t)stream));
+  return launched(dense_dispatch(M, ksplit_for(N, K), x, ml, out_dtype == W4A16_OUT_F32, K, group, (hipStream_t)stream));
 }
 
 w4a16_status_t w4a16_matmul_grouped(const uint16_t* x, const w4a16_matrix_t* mats, int count, int out_dtype, int M,
@@ -735,7 +759,7 @@ w4a16_status_t w4a16_matmul_grouped(const uint16_t* x, const w4a16_matrix_t* mat
         ml.m[ml.count++] = MatDesc{mats[i].qw, mats[i].scales, mats[i].biases, mats[i].y, mats[i].N};
         done[i] = true;
       }
-    const hipError_t e = dense_dispatch(M, ks, x, ml, out_dtype == W4A16_OUT_F32, K, (hipStream_t)stream);
+    const hipError_t e = dense_dispatch(M, ks, x, ml, out_dtype == W4A16_OUT_F32, K, group, (hipStream_t)stream);
     if (e != hipSuccess) return W4A16_ERR_HIP;
   }
   return W4A16_OK;
@@ -756,9 +780,14 @@ w4a16_status_t w4a16_matmul_id(const uint16_t* x, int x_per_slot, const uint32_t
   const int ks = ksplit_for(N, K);
   hipStream_t s = (hipStream_t)stream;
   // Without duplicate ids in a token, an expert serves at most M slots.
-  if (M == 1) return launched(routed_by_split<1>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
-  return launched(routed_by_split<kRoutedPassRows>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N,
-                                                   K, s));
+  if (group == 128) {
+    if (M == 1) return launched(routed_by_split<1, 128>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
+    return launched(routed_by_split<kRoutedPassRows, 128>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k,
+                                                          E, N, K, s));
+  }
+  if (M == 1) return launched(routed_by_split<1, 64>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E, N, K, s));
+  return launched(routed_by_split<kRoutedPassRows, 64>(ks, x, x_per_slot, qw, scales, biases, ids, y, f32, M, top_k, E,
+                                                       N, K, s));
 }
 
 size_t w4a16_lmhead_argmax_workspace_bytes(int M, int N, int K, int group) {
@@ -785,17 +814,8 @@ w4a16_status_t w4a16_lmhead_argmax(const uint16_t* x, const uint32_t* qw, const 
   hipStream_t s = (hipStream_t)stream;
   uint64_t* partial = reinterpret_cast<uint64_t*>(workspace);
   int nb = 0;
-  hipError_t e;
-  switch (M) {
-    case 1: e = lmhead_by_split<1>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-    case 2: e = lmhead_by_split<2>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-    case 3: e = lmhead_by_split<3>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-    case 4: e = lmhead_by_split<4>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-    case 5: e = lmhead_by_split<5>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-    case 6: e = lmhead_by_split<6>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-    case 7: e = lmhead_by_split<7>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-    default: e = lmhead_by_split<8>(ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb); break;
-  }
+  const hipError_t e = group == 128 ? lmhead_dispatch<128>(M, ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb)
+                                    : lmhead_dispatch<64>(M, ks, x, qw, scales, biases, logits, f32, partial, N, K, s, &nb);
   if (e != hipSuccess) return W4A16_ERR_HIP;
   hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(kFinalThreads), 0, s, partial, nb, M, argmax);
   return launched(hipGetLastError());
@@ -803,8 +823,8 @@ w4a16_status_t w4a16_lmhead_argmax(const uint16_t* x, const uint32_t* qw, const 
 
 w4a16_status_t w4a16_dequant(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, const int32_t* rows,
                              int R, float* out, int N, int K, int group, void* stream) {
-  if (group != 64) return W4A16_ERR_UNSUPPORTED;
-  if (N < 0 || K < 64 || K % 64 != 0) return W4A16_ERR_SHAPE;
+  if (!group_supported(group)) return W4A16_ERR_UNSUPPORTED;
+  if (N < 0 || K < group || K % group != 0) return W4A16_ERR_SHAPE;
   if (rows && R < 0) return W4A16_ERR_SHAPE;
   const int nrows = rows ? R : N;
   if (nrows == 0) return W4A16_OK;
@@ -816,14 +836,14 @@ w4a16_status_t w4a16_dequant(const uint32_t* qw, const uint16_t* scales, const u
   size_t blocks = (words + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, qw, scales,
-                     biases, rows, nrows, out, N, K);
+                     biases, rows, nrows, out, N, K, group == 128 ? 4 : 3);
   return launched(hipGetLastError());
 }
 
 w4a16_status_t w4a16_gather_rows(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
                                  const int32_t* rows, int R, uint16_t* out, int N, int K, int group, void* stream) {
-  if (group != 64) return W4A16_ERR_UNSUPPORTED;
-  if (N < 0 || R < 0 || K < 64 || K % 64 != 0) return W4A16_ERR_SHAPE;
+  if (!group_supported(group)) return W4A16_ERR_UNSUPPORTED;
+  if (N < 0 || R < 0 || K < group || K % group != 0) return W4A16_ERR_SHAPE;
   if (R == 0) return W4A16_OK;
   if (!qw || !scales || !biases || !rows || !out) return W4A16_ERR_NULL;
   if (!aligned(qw, 4) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(rows, 4) || !aligned(out, 16))
@@ -832,7 +852,7 @@ w4a16_status_t w4a16_gather_rows(const uint32_t* qw, const uint16_t* scales, con
   size_t blocks = (words + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, qw, scales, biases,
-                     rows, R, out, N, K);
+                     rows, R, out, N, K, group == 128 ? 4 : 3);
   return launched(hipGetLastError());
 }
 

@@ -10,7 +10,7 @@
  * "Group-Wise Affine Quantization", "Reconstruct a Stored Group" (w = q s + b,
  * unsigned 4-bit code, signed scale used as stored) and "Quantized Matrix
  * Multiplication" (C = A B^T with the dequantized B), at the group size 64 of
- * the Gemma-4 megakernel page ("Usage").  M is 1 for greedy decode or k+1 for
+ * the Gemma-4 megakernel page ("Usage") or the tiny-llm page's 128.  M is 1 for greedy decode or k+1 for
  * a speculative-verify batch (Gemma-4 megakernel page, "What it does": the
  * weights stream once for all M rows).
  *
@@ -41,7 +41,8 @@
  *   - Empty problems (M == 0 or N == 0) succeed without launching.
  *   - Alignment: qw and x 16 bytes; scales, biases 2 bytes; y 2 bytes
  *     (bf16) or 4 bytes (fp32); ids, argmax 4 bytes; workspace 8 bytes.
- *   - Only group == 64 and 4-bit codes are supported.
+ *   - 4-bit codes with group == 64 (the workload's) or group == 128 (the
+ *     tiny-llm page's); K must be a multiple of the group.
  *   - Asynchronous device faults surface at the caller's next synchronization.
  */
 #ifndef W4A16_H
@@ -77,7 +78,8 @@ typedef enum w4a16_out {
 /*
  * Dense product, 1 <= M <= 8 (qmv at M = 1, skinny qmm at M = 2..8).
  * Definition: "Quantized Matrix Multiplication" / "Computation Flow" on the
- * tiny-llm W4 page, with the group size of the Gemma-4 page.
+ * tiny-llm W4 page, with the group size of the Gemma-4 page (64) or of the
+ * tiny-llm page (128).
  * y: [M][N], bf16 or fp32 per out_dtype.
  */
 w4a16_status_t w4a16_matmul(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
@@ -189,10 +191,11 @@ const char *w4a16_status_str(w4a16_status_t s);
 
 /*
  * Name of the kernel instantiation w4a16_matmul launches for this shape, as
- * profilers report it ("qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS>":
+ * profilers report it ("qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>":
  * activation rows, rows per lane, 16-byte chunks per lane per K-tile, waves
  * sharing a row, chunk slots whose loads are issued before the activations are
- * staged, chunk slots in flight per lane, row sets per block when KSPLIT > 1).
+ * staged, chunk slots in flight per lane, row sets per block when KSPLIT > 1,
+ * group size).
  * "" when the arguments are invalid.  The string lives in thread-local storage
  * and stays valid until the next call on the same thread.
  */

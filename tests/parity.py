@@ -57,7 +57,7 @@ def oracle_qmm(orc, x, w, rows=None, workers=8):
     idx = np.arange(N, dtype=np.int32) if rows is None else np.asarray(rows, dtype=np.int32)
     parts = np.array_split(idx, min(workers, max(1, len(idx))))
     with cf.ThreadPoolExecutor(len(parts)) as ex:
-        res = list(ex.map(lambda r: orc.qmm(x, w.qw, w.scales, w.biases, rows=r), parts))
+        res = list(ex.map(lambda r: orc.qmm(x, w.qw, w.scales, w.biases, group=w.group, rows=r), parts))
     y = np.concatenate([r[0] for r in res], axis=1)
     a = np.concatenate([r[1] for r in res], axis=1)
     return y, a

@@ -53,8 +53,9 @@ def mm(L, x=A16, qw=A16, s=A16, b=A16, y=A16, out=0, M=1, N=256, K=512, group=64
 
 
 def test_matmul_rejects_bad_arguments(L):
-    assert mm(L, group=128) == EUNSUP
     assert mm(L, group=32) == EUNSUP
+    assert mm(L, group=256) == EUNSUP
+    assert mm(L, group=128, K=192) == ESHAPE          # K must be a multiple of the group
     assert mm(L, out=2) == EUNSUP
     assert mm(L, M=9) == EUNSUP
     assert mm(L, M=-1) == ESHAPE
@@ -125,7 +126,8 @@ def test_lmhead_workspace_rules(L):
     ws = L.w4a16_lmhead_argmax_workspace_bytes
     assert ws(1, 262144, 2560, 64) > 0
     assert ws(3, 262144, 2560, 64) >= ws(1, 262144, 2560, 64)
-    assert ws(1, 262144, 2560, 128) == 0
+    assert ws(1, 262144, 2560, 32) == 0
+    assert ws(1, 1000, 2560, 128) == ws(1, 1000, 2560, 64) > 0
     assert ws(1, 262144, 100, 64) == 0
     assert ws(0, 262144, 2560, 64) == 0
     need = ws(1, 1000, 512, 64)

@@ -168,13 +168,14 @@ def test_dequant_is_one_fp32_rounding_of_the_exact_value(orc):
             assert got == want, (hex(s), hex(b), q)
 
 
-def test_dequant_rows_brute_force(orc):
-    wts = synthetic.quantized_weights(5, 128, seed=6)
-    out = orc.dequant_rows(wts.qw, wts.scales, wts.biases, 128, rows=[4, 0, 2])
-    codes = orc.unpack_rows(wts.qw, 128)
+@pytest.mark.parametrize("G", [64, 128])
+def test_dequant_rows_brute_force(orc, G):
+    wts = synthetic.quantized_weights(5, 256, group=G, seed=6)
+    out = orc.dequant_rows(wts.qw, wts.scales, wts.biases, 256, group=G, rows=[4, 0, 2])
+    codes = orc.unpack_rows(wts.qw, 256)
     for r, n in enumerate([4, 0, 2]):
-        for k in range(0, 128, 7):
-            g = k // 64
+        for k in range(0, 256, 7):
+            g = k // G
             exact = bf16_fraction(int(wts.scales[n, g])) * int(codes[n, k]) + bf16_fraction(int(wts.biases[n, g]))
             assert Fraction(float(out[r, k])) == to_f32(exact)
 
@@ -183,28 +184,30 @@ def test_dequant_rows_brute_force(orc):
 # The product: closed forms ("Quantized Matrix Multiplication" equations)
 # ---------------------------------------------------------------------------
 
-def _scales_biases(N, K, seed, bias="noise"):
-    w = synthetic.quantized_weights(N, K, seed=seed, bias=bias)
+def _scales_biases(N, K, seed, bias="noise", group=64):
+    w = synthetic.quantized_weights(N, K, group=group, seed=seed, bias=bias)
     return w.scales, w.biases
 
 
+@pytest.mark.parametrize("G", [64, 128])
 @pytest.mark.parametrize("c", [0, 1, 7, 8, 15])
-def test_cf1_all_codes_equal(orc, c):
-    # all codes = c: y = sum_g (s_g c + b_g) * sum_{k in g} x_k
-    N, K, M = 6, 320, 2
+def test_cf1_all_codes_equal(orc, c, G):
+    # all codes = c: y = sum_g (s_g c + b_g) * sum_{k in g} x_k, groups of G codes
+    N, K, M = 6, 384, 2
     codes = np.full((N, K), c, dtype=np.uint8)
     qw = packed(orc, codes)
-    s, b = _scales_biases(N, K, seed=7)
+    s, b = _scales_biases(N, K, seed=7, group=G)
+    assert s.shape == (N, K // G)
     x = synthetic.activations(M, K, seed=7)
-    y, _ = orc.qmm(x, qw, s, b)
+    y, _ = orc.qmm(x, qw, s, b, group=G)
     for m in range(M):
         xs = [bf16_fraction(int(v)) for v in x[m]]
         for n in range(N):
             want = Fraction(0)
-            for g in range(K // 64):
+            for g in range(K // G):
                 wg = bf16_fraction(int(s[n, g])) * c + bf16_fraction(int(b[n, g]))
                 assert to_f32(wg) == wg          # exact in fp32 for these values
-                want += wg * sum(xs[64 * g:64 * g + 64])
+                want += wg * sum(xs[G * g:G * g + G])
             assert abs(Fraction(y[m, n]) - want) <= Fraction(1, 2 ** 45) * (abs(want) + 1)
 
 
@@ -301,16 +304,17 @@ def test_cf7_exact_bias_distribution_is_exact(orc):
 
 
 def test_brute_force_against_exact_rationals(orc):
-    for (M, N, K, seed) in [(1, 3, 64, 20), (2, 16, 128, 21), (3, 5, 192, 22)]:
-        wts = synthetic.quantized_weights(N, K, seed=seed)
+    for (M, N, K, G, seed) in [(1, 3, 64, 64, 20), (2, 16, 128, 64, 21), (3, 5, 192, 64, 22), (2, 7, 256, 128, 24),
+                               (1, 4, 384, 128, 25)]:
+        wts = synthetic.quantized_weights(N, K, group=G, seed=seed)
         x = synthetic.activations(M, K, seed=seed)
-        y, a = orc.qmm(x, wts.qw, wts.scales, wts.biases)
+        y, a = orc.qmm(x, wts.qw, wts.scales, wts.biases, group=G)
         codes = orc.unpack_rows(wts.qw, K)
         for m in range(M):
             xs = [bf16_fraction(int(v)) for v in x[m]]
             for n in range(N):
-                ws = [to_f32(bf16_fraction(int(wts.scales[n, k // 64])) * int(codes[n, k])
-                             + bf16_fraction(int(wts.biases[n, k // 64]))) for k in range(K)]
+                ws = [to_f32(bf16_fraction(int(wts.scales[n, k // G])) * int(codes[n, k])
+                             + bf16_fraction(int(wts.biases[n, k // G]))) for k in range(K)]
                 want = sum(xv * wv for xv, wv in zip(xs, ws))
                 absw = sum(abs(xv * wv) for xv, wv in zip(xs, ws))
                 assert abs(Fraction(y[m, n]) - want) <= Fraction(K, 2 ** 52) * absw

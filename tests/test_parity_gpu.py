@@ -466,3 +466,76 @@ def test_routed_variants(orc):
     keep = np.ones((M, top_k), dtype=bool)
     keep[1, 1] = keep[4, 0] = False
     assert np.array_equal(yb[keep].view(np.uint32), y[keep].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Group size 128 (the tiny-llm page's group): same kernels, scales and biases
+# per 128 codes
+# ---------------------------------------------------------------------------
+
+def run_mm_g(dw, x_bits, N, group, f32=False):
+    x = dev_bf16(x_bits)
+    y = torch.empty((x.shape[0], N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    w4.w4a16_matmul(x, dw.qw, dw.s, dw.b, y, group=group)
+    torch.cuda.synchronize()
+    return host_f32(y) if f32 else host_bits(y)
+
+
+# one case per schedule class: tiny, one-chunk K-split, long-row K-split (two
+# row sets from M = 2), one row group per row, several K-tiles (double
+# buffered at M = 1), N >= 16384 with K % 2560 == 0
+G128 = [(8, 128), (300, 2560), (1003, 6272), (4097, 768), (4200, 5120), (16400, 2560)]
+
+
+@pytest.mark.parametrize("N,K", G128)
+def test_group128_every_M_batch_invariant(orc, N, K):
+    w = synthetic.quantized_weights(N, K, group=128, seed=N + K)
+    x = synthetic.activations(8, K, seed=N + K + 1)
+    say(f"group 128 N={N} K={K}: oracle")
+    y64, absy = oracle_qmm(orc, x, w)
+    dw = DevWeights(w)
+    ref32 = [run_mm_g(dw, x[m:m + 1], N, 128, f32=True)[0] for m in range(8)]
+    for M in range(1, 9):
+        say(f"  group 128 N={N} K={K} M={M}")
+        y32 = run_mm_g(dw, x[:M], N, 128, f32=True)
+        check_f32(y32, y64[:M], absy[:M], f"G=128 N={N} K={K} M={M}")
+        yb = run_mm_g(dw, x[:M], N, 128)
+        check_bf16(orc, yb, y64[:M], absy[:M], K, f"G=128 N={N} K={K} M={M}")
+        assert np.array_equal(yb, synthetic.bf16_bits(y32))
+        for m in range(M):
+            assert np.array_equal(y32[m].view(np.uint32), ref32[m].view(np.uint32)), (N, K, M, m)
+
+
+def test_group128_routed_lmhead_dequant_gather(orc):
+    say("group 128: routed product")
+    E, N, K, M, top_k = 4, 700, 1024, 3, 2
+    w = synthetic.quantized_weights(N, K, group=128, seed=31, lead=(E,))
+    x = synthetic.activations(M, K, seed=31)
+    ids = np.array([[0, 3], [3, 1], [2, 2]], dtype=np.int32)
+    y64, absy = orc.qmm_id(x, w.qw, w.scales, w.biases, ids, group=128)
+    y = w4.matmul_id(dev_bf16(x), dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases), dev_i32(ids),
+                     out_dtype=torch.float32, group=128)
+    torch.cuda.synchronize()
+    check_f32(host_f32(y), y64, absy, "G=128 routed")
+
+    say("group 128: LM head with argmax")
+    N, K, M = 5000, 2560, 3
+    w = synthetic.quantized_weights(N, K, group=128, seed=32, bias="exact")
+    x = synthetic.activations(M, K, seed=32)
+    y64, absy = oracle_qmm(orc, x, w)
+    am, logits = w4.lmhead_argmax(dev_bf16(x), dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases),
+                                  out_dtype=torch.float32, group=128)
+    torch.cuda.synchronize()
+    check_f32(host_f32(logits), y64, absy, "G=128 LM head")
+    assert check_argmax(orc, am.cpu().numpy(), y64, absy, "G=128 LM head") >= 1   # rows whose top-2 gap exceeds the bound
+
+    say("group 128: dequant and row gather")
+    w = synthetic.quantized_weights(50, 640, group=128, seed=33)
+    ref = orc.dequant_rows(w.qw, w.scales, w.biases, 640, group=128)
+    got = w4.dequant(dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases), group=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(got).view(np.uint32), ref.view(np.uint32))
+    rows = np.array([49, 0, 7, 7, 50], dtype=np.int32)
+    g = host_bits(w4.gather_rows(dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases), dev_i32(rows), group=128))
+    assert np.array_equal(g[:4], orc.f64_to_bf16(ref[[49, 0, 7, 7]].astype(np.float64)))
+    assert (g[4] == 0x7FC0).all()

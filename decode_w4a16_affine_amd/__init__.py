@@ -29,7 +29,7 @@ MAX_M = 8
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN",
           5: "ERR_WORKSPACE", 6: "ERR_HIP"}
 
-EXPORTS = ("w4a16_matmul", "w4a16_matmul_grouped", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
+EXPORTS = ("w4a16_matmul", "w4a16_matmul_prefill", "w4a16_matmul_grouped", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
            "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_gather_rows", "w4a16_pack", "w4a16_status_str",
            "w4a16_abi_version", "w4a16_schedule_name")
 
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.w4a16_matmul.restype = _int
         L.w4a16_matmul.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]
+        L.w4a16_matmul_prefill.restype = _int
+        L.w4a16_matmul_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]
         L.w4a16_matmul_grouped.restype = _int
         L.w4a16_matmul_grouped.argtypes = [_vp, ctypes.POINTER(Matrix), _int, _int, _int, _int, _int, _vp]
         L.w4a16_matmul_id.restype = _int
@@ -137,6 +139,15 @@ def w4a16_matmul(x, qw, scales, biases, y, group: int = GROUP, stream=None) -> N
     N = qw.shape[0]
     _check(lib().w4a16_matmul(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(y), _out_code(y),
                               M, N, K, group, _stream(stream)), "w4a16_matmul")
+
+
+def w4a16_matmul_prefill(x, qw, scales, biases, y, group: int = GROUP, stream=None) -> None:
+    """y[M,N] = x[M,K] . W^T for prefill-sized M (matrix cores; not bitwise equal to w4a16_matmul)."""
+    _dtype(x, torch.bfloat16, "x"); _dtype(qw, torch.int32, "qw")
+    M, K = x.shape
+    N = qw.shape[0]
+    _check(lib().w4a16_matmul_prefill(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(y), _out_code(y),
+                                      M, N, K, group, _stream(stream)), "w4a16_matmul_prefill")
 
 
 def w4a16_matmul_grouped(x, mats, group: int = GROUP, stream=None) -> None:
@@ -227,6 +238,12 @@ def w4a16_schedule_name(M: int, N: int, K: int, group: int = GROUP) -> str:
 def matmul(x, qw, scales, biases, out_dtype=torch.bfloat16, group: int = GROUP, stream=None):
     y = torch.empty((x.shape[0], qw.shape[0]), dtype=out_dtype, device=x.device)
     w4a16_matmul(x, qw, scales, biases, y, group=group, stream=stream)
+    return y
+
+
+def matmul_prefill(x, qw, scales, biases, out_dtype=torch.bfloat16, group: int = GROUP, stream=None):
+    y = torch.empty((x.shape[0], qw.shape[0]), dtype=out_dtype, device=x.device)
+    w4a16_matmul_prefill(x, qw, scales, biases, y, group=group, stream=stream)
     return y
 
 

@@ -8,6 +8,7 @@
 #include <type_traits>
 
 #include "qmm_device.hpp"
+#include "qmm_prefill.hpp"
 #include "w4a16.h"
 
 using namespace w4k;
@@ -726,6 +727,42 @@ w4a16_status_t w4a16_matmul(const uint16_t* x, const uint32_t* qw, const uint16_
   ml.m[0] = MatDesc{qw, scales, biases, y, N};
   ml.count = 1;
   return launched(dense_dispatch(M, ksplit_for(N, K), x, ml, out_dtype == W4A16_OUT_F32, K, group, (hipStream_t)stream));
+}
+
+w4a16_status_t w4a16_matmul_prefill(const uint16_t* x, const uint32_t* qw, const uint16_t* scales,
+                                    const uint16_t* biases, void* y, int out_dtype, int M, int N, int K, int group,
+                                    void* stream) {
+  if (M < 0 || M > W4A16_MAX_PREFILL_M) return M < 0 ? W4A16_ERR_SHAPE : W4A16_ERR_UNSUPPORTED;
+  w4a16_status_t st = check_shape(0, N, K, group, out_dtype);
+  if (st != W4A16_OK) return st;
+  if (M == 0 || N == 0) return W4A16_OK;
+  st = check_weights(x, qw, scales, biases, y, out_dtype);
+  if (st != W4A16_OK) return st;
+  // Tiles of 64 activation rows x 32 weight rows per wave; when fewer than
+  // 1024 such tiles exist, the four waves of a block split K of one tile.
+  constexpr int TM = 4, TN = 2;
+  const long tiles = (long)((M + 16 * TM - 1) / (16 * TM)) * ((N + 16 * TN - 1) / (16 * TN));
+  const bool ksplit = tiles < 1024;
+  const int cols = ksplit ? 16 * TN : kPrefillWaves * 16 * TN;
+  const dim3 grid((unsigned)((N + cols - 1) / cols), (unsigned)((M + 16 * TM - 1) / (16 * TM)));
+  const int f32 = out_dtype == W4A16_OUT_F32;
+  hipStream_t s = (hipStream_t)stream;
+  if (group == 128) {
+    if (ksplit)
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 128>), grid, dim3(kPrefillWaves * kWave), 0, s,
+                         x, qw, scales, biases, y, M, N, K, f32);
+    else
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 128>), grid, dim3(kPrefillWaves * kWave), 0, s, x, qw,
+                         scales, biases, y, M, N, K, f32);
+  } else {
+    if (ksplit)
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 64>), grid, dim3(kPrefillWaves * kWave), 0, s,
+                         x, qw, scales, biases, y, M, N, K, f32);
+    else
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 64>), grid, dim3(kPrefillWaves * kWave), 0, s, x, qw,
+                         scales, biases, y, M, N, K, f32);
+  }
+  return launched(hipGetLastError());
 }
 
 w4a16_status_t w4a16_matmul_grouped(const uint16_t* x, const w4a16_matrix_t* mats, int count, int out_dtype, int M,

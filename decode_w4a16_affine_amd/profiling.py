@@ -20,7 +20,8 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(HERE, "csrc", "qmm_device.hpp"), os.path.join(HERE, "csrc", "w4a16.hip")]
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", "qmm_device.hpp"), os.path.join(HERE, "csrc", "qmm_prefill.hpp"),
+                  os.path.join(HERE, "csrc", "w4a16.hip")]
 COPY_BYTES = 256 << 20
 
 
@@ -34,7 +35,8 @@ def kernel_source_sha() -> str:
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(qmm_\w+_kernel<[^>]*>|argmax_finalize_kernel|dequant_rows_kernel|pack_kernel)", name)
+    m = re.search(r"(qmm_\w+_kernel<[^>]*>|argmax_finalize_kernel|dequant_rows_kernel|gather_rows_kernel|pack_kernel)",
+                  name)
     return m.group(1) if m else name.split("(")[0][:80]
 
 

@@ -57,6 +57,7 @@ extern "C" {
 
 #define W4A16_ABI_VERSION 1
 #define W4A16_MAX_M 8
+#define W4A16_MAX_PREFILL_M 65536
 #define W4A16_MAX_GROUP 8
 
 typedef enum w4a16_status {
@@ -85,6 +86,19 @@ typedef enum w4a16_out {
 w4a16_status_t w4a16_matmul(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
                             const uint16_t *biases, void *y, int out_dtype, int M, int N, int K,
                             int group, void *stream);
+
+/*
+ * Prefill-shaped product, 1 <= M <= W4A16_MAX_PREFILL_M activation rows (a
+ * prompt's tokens): the same y = x W^T and dequantization as w4a16_matmul,
+ * computed on the matrix cores (tiny-llm page, "Revisit the Decode Roofline":
+ * prefill reuses each weight across many rows and needs a matrix schedule).
+ * Each fp32 weight fma(s, q, b) enters as bf16 hi + lo parts, so the result
+ * stays within the same error bound, but its summation order differs from the
+ * M <= 8 schedules: no bitwise equality with w4a16_matmul.  Meant for M > 8.
+ */
+w4a16_status_t w4a16_matmul_prefill(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
+                                    const uint16_t *biases, void *y, int out_dtype, int M, int N,
+                                    int K, int group, void *stream);
 
 /*
  * One matrix of a grouped product: packed weights, scales, biases and its

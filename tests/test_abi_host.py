@@ -74,6 +74,20 @@ def test_matmul_rejects_bad_arguments(L):
     assert mm(L, y=A16 + 2, out=1) == EALIGN  # fp32 output needs 4 bytes
 
 
+def test_prefill_rejects_bad_arguments(L):
+    def pf(x=A16, qw=A16, y=A16, out=0, M=100, N=256, K=512, group=64):
+        return L.w4a16_matmul_prefill(x, qw, A16, A16, y, out, M, N, K, group, None)
+    assert pf(M=-1) == ESHAPE
+    assert pf(M=65537) == EUNSUP
+    assert pf(group=32) == EUNSUP
+    assert pf(K=100) == ESHAPE
+    assert pf(x=A4) == EALIGN
+    assert pf(qw=None) == ENULL
+    assert pf(out=7) == EUNSUP
+    assert pf(x=None, qw=None, y=None, M=0) == OK
+    assert pf(x=None, qw=None, y=None, N=0) == OK
+
+
 def test_matmul_empty_problems_launch_nothing(L):
     # empty problems succeed even with NULL pointers: nothing is read or written
     assert mm(L, x=None, qw=None, s=None, b=None, y=None, M=0) == OK

@@ -539,3 +539,49 @@ def test_group128_routed_lmhead_dequant_gather(orc):
     g = host_bits(w4.gather_rows(dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases), dev_i32(rows), group=128))
     assert np.array_equal(g[:4], orc.f64_to_bf16(ref[[49, 0, 7, 7]].astype(np.float64)))
     assert (g[4] == 0x7FC0).all()
+
+
+# ---------------------------------------------------------------------------
+# Prefill-shaped product (M > 8) on the matrix cores
+# ---------------------------------------------------------------------------
+
+def run_prefill(dw, x_bits, N, group=64, f32=False):
+    x = dev_bf16(x_bits)
+    y = torch.empty((x.shape[0], N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    w4.w4a16_matmul_prefill(x, dw.qw, dw.s, dw.b, y, group=group)
+    torch.cuda.synchronize()
+    return host_f32(y) if f32 else host_bits(y)
+
+
+# ragged M, N and K, both group sizes, tiles and tails in every dimension
+PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 4097, 1024, 64), (64, 128, 64, 64),
+           (70, 513, 1280, 128), (1, 77, 256, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,G", PREFILL)
+def test_prefill_matches_oracle(orc, M, N, K, G):
+    w = synthetic.quantized_weights(N, K, group=G, seed=M + N + K)
+    x = synthetic.activations(M, K, seed=M * 3 + K)
+    rows = np.arange(0, N, max(1, N // 300), dtype=np.int32)
+    say(f"prefill M={M} N={N} K={K} G={G}: oracle on {len(rows)} rows")
+    y64, absy = oracle_qmm(orc, x, w, rows=rows)
+    dw = DevWeights(w)
+    y32 = run_prefill(dw, x, N, G, f32=True)
+    rel = check_f32(y32[:, rows], y64, absy, f"prefill M={M} N={N} K={K}")
+    yb = run_prefill(dw, x, N, G)
+    ex = check_bf16(orc, yb[:, rows], y64, absy, K, f"prefill M={M} N={N} K={K}")
+    say(f"  max |err|/sum|wx| = {rel:.2e}, bf16 exempt {ex}")
+    assert np.array_equal(yb, synthetic.bf16_bits(y32))
+    assert np.array_equal(run_prefill(dw, x, N, G, f32=True).view(np.uint32), y32.view(np.uint32))   # deterministic
+
+
+def test_prefill_crafted_scales(orc):
+    # signs, zero, subnormal and |s| >= 2^100 scales (the plain dequant path)
+    M, N, K = 20, 64, 2560
+    w = synthetic.quantized_weights(N, K, seed=41)
+    w.scales, w.biases = crafted_scales(N, K // 64, seed=41)
+    x = synthetic.activations(M, K, seed=41)
+    say("prefill crafted scales")
+    y64, absy = oracle_qmm(orc, x, w)
+    y32 = run_prefill(DevWeights(w), x, N, f32=True)
+    check_f32(y32, y64, absy, "prefill crafted")

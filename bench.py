@@ -34,6 +34,8 @@ import synthetic  # noqa: E402
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) for W4A16 qmv M=1 and qmm M=k+1"
 PEAK_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
+PREFILL_M = (512, 4096)
 LAYERS = 42
 # untimed replay time before each measurement (beyond the warm-up count): the
 # first measurement runs the step for a second so the clocks have settled
@@ -279,6 +281,30 @@ def config_timings(torch, w4, reps: int = 5):
         out["square"][str(M)] = timed(calls, call_bytes(M, N, K))
     del qw, sc, bi
     log(f"square: {out['square']}")
+
+    # prefill-sized products (w4a16_matmul_prefill, matrix cores) on the decode
+    # stack's gate+up and down shapes: flop-bound, so priced against the dense
+    # bf16 matrix-core peak.  Algorithmic flops are 2*M*N*K; the matrix cores
+    # execute twice that (every weight enters as a bf16 high and low part).
+    out["prefill"] = {}
+    for name in ("gate_up", "down"):
+        N, K = synthetic.PROJECTIONS[name]
+        w = synthetic.quantized_weights(N, K, seed=0, tag=(N, 7))
+        qw, sc, bi = upload(w, 2)
+        del w
+        out["prefill"][name] = {}
+        for M in PREFILL_M:
+            x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(N, 7)).view(np.int16)).view(torch.bfloat16).cuda()
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            calls = [lambda c=c: w4.w4a16_matmul_prefill(x, qw[c], sc[c], bi[c], y) for c in (0, 1)]
+            r = timed(calls, call_bytes(M, N, K))
+            tflops = 2.0 * M * N * K / (r["us"] * 1e-6) / 1e12
+            r.update(tflops=round(tflops, 1), mfma_tflops=round(2 * tflops, 1),
+                     frac_of_bf16_peak=round(tflops / PEAK_BF16_TFLOPS, 4))
+            out["prefill"][name][str(M)] = r
+            del x, y
+        del qw, sc, bi
+    log(f"prefill: {out['prefill']}")
 
     # routed MoE stack: 64 experts, top-8 of 64 per token
     t = synthetic.MOE

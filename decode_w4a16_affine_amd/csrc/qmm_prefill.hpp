@@ -176,4 +176,178 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// LDS-tiled form for large M.  A block of 2 * BM / 64 waves owns a BM x 128
+// output tile (BM = 128 or 256) and walks K in steps of 64 codes.  Per step the
+// block stages the activation tile (BM rows x 64 bf16) and the weight tile,
+// dequantized once (128 rows x 64 weights, each split into its bf16 hi and lo
+// parts), in LDS; each wave then multiplies a 64 x 64 piece from LDS (4 x 4
+// fragments of 16 x 16, two K halves, hi and lo: 64 matrix instructions per
+// step).  So every weight is dequantized once per BM activation rows and every
+// activation is fetched once per 128 weight rows.  The next step's global
+// loads are in flight while the current step computes.  LDS rows hold 72 bf16
+// (144 bytes): the 16 lanes of a fragment read rows 144 bytes apart, on
+// distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kPfBN = 128, kPfBK = 64;
+constexpr int kPfStr = kPfBK + 8;   // bf16 per LDS row
+template <int BM>
+constexpr int kPfThreads = 2 * BM;
+
+// Block -> output tile.  Workgroups go to the eight XCDs (each with its own
+// L2) in turn, so block b runs on XCD b % 8; giving each XCD a contiguous run
+// of tiles (row-major over 128 x 128 tiles) lets its blocks share activation
+// tiles in their L2.
+__device__ __forceinline__ int prefill_tile_of(int b, int nb) {
+  if (nb % 8 != 0) return b;
+  return (b % 8) * (nb / 8) + b / 8;
+}
+
+// One K step's global operands of a thread (kept as separate values: arrays
+// or structs of them were placed in LDS by the compiler): four 16-byte
+// activation pieces, WPT packed weight words (WPT == 2 uses .x, .y), and the
+// group's scale and bias bits.
+template <int WPT, int G>
+__device__ __forceinline__ void pf_load(uint4& a0, uint4& a1, uint4& a2, uint4& a3, uint4& w, uint32_t& s,
+                                        uint32_t& b, const uint16_t* x0, const uint16_t* x1, const uint16_t* x2,
+                                        const uint16_t* x3, const uint32_t* wq, const uint16_t* ws,
+                                        const uint16_t* wb, int k0, int bq) {
+  a0 = *reinterpret_cast<const uint4*>(x0 + k0);
+  a1 = *reinterpret_cast<const uint4*>(x1 + k0);
+  a2 = *reinterpret_cast<const uint4*>(x2 + k0);
+  a3 = *reinterpret_cast<const uint4*>(x3 + k0);
+  if constexpr (WPT == 4) {
+    w = *reinterpret_cast<const uint4*>(wq + (k0 >> 3));
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(wq + (k0 >> 3));
+    w = make_uint4(v.x, v.y, 0u, 0u);
+  }
+  const int g = (k0 + 8 * WPT * bq) / G;
+  s = ws[g];
+  b = wb[g];
+}
+
+// activations and the dequantized hi/lo weights of one step into LDS
+template <int WPT>
+__device__ __forceinline__ void pf_stage(const uint4& a0, const uint4& a1, const uint4& a2, const uint4& a3,
+                                         const uint4& w, uint32_t s, uint32_t b, uint16_t* As, uint16_t* Bh,
+                                         uint16_t* Bl, int ao0, int ao1, int ao2, int ao3, int boff) {
+  *reinterpret_cast<uint4*>(As + ao0) = a0;
+  *reinterpret_cast<uint4*>(As + ao1) = a1;
+  *reinterpret_cast<uint4*>(As + ao2) = a2;
+  *reinterpret_cast<uint4*>(As + ao3) = a3;
+  const float sv = bf16_lo(s), bv = bf16_lo(b);
+  const bool plain = needs_plain(sv);
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const uint32_t word = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+    float d[8];
+    if (plain)
+      dequant8_plain(word, sv, bv, d);
+    else
+      dequant8_fast(word, sv * 0x1p24f, sv * 0x1p20f, bv, d);
+    bf16x8_t hi, lo;
+    split_bf16(d, hi, lo);
+    *reinterpret_cast<bf16x8_t*>(Bh + boff + 8 * j) = hi;
+    *reinterpret_cast<bf16x8_t*>(Bl + boff + 8 * j) = lo;
+  }
+}
+
+// a wave's 64 x 64 piece of one staged step: per K half, its four activation
+// fragments, then per 16-row weight tile the hi and lo fragments (8 matrix
+// instructions each)
+__device__ __forceinline__ void pf_compute(f32x4_t (&acc)[4][4], const uint16_t* As, const uint16_t* Bh,
+                                           const uint16_t* Bl, int arow, int brow, int lk) {
+#pragma unroll
+  for (int ks = 0; ks < kPfBK / 32; ++ks) {
+    bf16x8_t a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      a[t] = *reinterpret_cast<const bf16x8_t*>(As + (arow + t * 16) * kPfStr + ks * 32 + 8 * lk);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = (brow + u * 16) * kPfStr + ks * 32 + 8 * lk;
+      const bf16x8_t h = *reinterpret_cast<const bf16x8_t*>(Bh + o);
+      const bf16x8_t l = *reinterpret_cast<const bf16x8_t*>(Bl + o);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], h, acc[t][u], 0, 0, 0);
+        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], l, acc[t][u], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int BM, int G>
+__global__ __launch_bounds__(kPfThreads<BM>) void qmm_prefill_tiled_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, void* __restrict__ y, int M, int N, int K, int out_f32, int tiles_n) {
+  constexpr int NT = kPfThreads<BM>;
+  constexpr int WPT = kPfBN * (kPfBK / 8) / NT;   // packed words of the weight tile per thread (4 or 2)
+  constexpr int TPR = (kPfBK / 8) / WPT;          // threads per weight row
+  static_assert(BM == 128 || BM == 256, "block height");
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * kPfStr];
+  __shared__ __attribute__((aligned(16))) uint16_t Bh[kPfBN * kPfStr];
+  __shared__ __attribute__((aligned(16))) uint16_t Bl[kPfBN * kPfStr];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tile = prefill_tile_of((int)blockIdx.x, (int)gridDim.x);
+  const int m0 = tile / tiles_n * BM, n0 = tile % tiles_n * kPfBN;
+
+  // staging: activation piece p = tid + NT i (row p / 8, 16-byte column p % 8);
+  // weight row tid / TPR, words WPT (tid % TPR) .. +WPT-1 of the step (one
+  // 16- or 8-byte load).  Rows past M or N are clamped (in-bounds loads, never
+  // stored).
+  auto xrow = [&](int i) { return x + (size_t)min(m0 + (tid + NT * i) / 8, M - 1) * K + 8 * (tid % 8); };
+  auto aofs = [&](int i) { return (tid + NT * i) / 8 * kPfStr + 8 * (tid % 8); };
+  const uint16_t *x0 = xrow(0), *x1 = xrow(1), *x2 = xrow(2), *x3 = xrow(3);
+  const int ao0 = aofs(0), ao1 = aofs(1), ao2 = aofs(2), ao3 = aofs(3);
+  const int br = tid / TPR, bq = tid % TPR;
+  const size_t bn = (size_t)min(n0 + br, N - 1);
+  const uint32_t* wq = qw + bn * (size_t)(K >> 3) + WPT * bq;
+  const uint16_t* ws = scales + bn * (size_t)(K / G);
+  const uint16_t* wb = biases + bn * (size_t)(K / G);
+  const int boff = br * kPfStr + 8 * WPT * bq;
+
+  const int wm = wave >> 1, wn = wave & 1;   // this wave's 64 x 64 piece
+  const int li = lane & 15, lk = lane >> 4;
+  const int arow = wm * 64 + li, brow = wn * 64 + li;
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // the next step's global loads are in flight while the current one computes
+  const int steps = K / kPfBK;
+  uint4 a0, a1, a2, a3, w;
+  uint32_t s, b;
+  pf_load<WPT, G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
+  for (int st = 0; st < steps; ++st) {
+    __syncthreads();   // every wave is done reading the previous step's tiles
+    pf_stage<WPT>(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
+    __syncthreads();
+    if (st + 1 < steps) pf_load<WPT, G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
+    pf_compute(acc, As, Bh, Bl, arow, brow, lk);
+  }
+
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = n0 + wn * 64 + u * 16 + li;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 64 + t * 16 + 4 * lk + i;
+        if (m < M && n < N) {
+          if (out_f32)
+            reinterpret_cast<float*>(y)[(size_t)m * N + n] = acc[t][u][i];
+          else
+            reinterpret_cast<uint16_t*>(y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16(acc[t][u][i]);
+        }
+      }
+    }
+}
+
 }  // namespace w4k

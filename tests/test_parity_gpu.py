@@ -553,9 +553,13 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
     return host_f32(y) if f32 else host_bits(y)
 
 
-# ragged M, N and K, both group sizes, tiles and tails in every dimension
+# ragged M, N and K, both group sizes, tiles and tails in every dimension.  The
+# LDS-tiled form (128 x 128 tiles) runs where its grid has >= 256 blocks:
+# 300 x 12837, 520 x 16390 and 256 x 32768 (a grid permuted across the XCDs);
+# the other shapes run the per-wave form.
 PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 4097, 1024, 64), (64, 128, 64, 64),
-           (70, 513, 1280, 128), (1, 77, 256, 128)]
+           (70, 513, 1280, 128), (1, 77, 256, 128), (520, 2560, 2560, 64), (300, 12837, 640, 128),
+           (520, 16390, 512, 64), (256, 32768, 256, 64)]
 
 
 @pytest.mark.parametrize("M,N,K,G", PREFILL)
@@ -575,13 +579,16 @@ def test_prefill_matches_oracle(orc, M, N, K, G):
     assert np.array_equal(run_prefill(dw, x, N, G, f32=True).view(np.uint32), y32.view(np.uint32))   # deterministic
 
 
-def test_prefill_crafted_scales(orc):
-    # signs, zero, subnormal and |s| >= 2^100 scales (the plain dequant path)
-    M, N, K = 20, 64, 2560
+@pytest.mark.parametrize("M,N,K", [(20, 64, 2560), (200, 32768, 256)])
+def test_prefill_crafted_scales(orc, M, N, K):
+    # signs, zero, subnormal and |s| >= 2^100 scales (the plain dequant path),
+    # in the per-wave (M = 20) and the LDS-tiled (M = 200) forms
     w = synthetic.quantized_weights(N, K, seed=41)
     w.scales, w.biases = crafted_scales(N, K // 64, seed=41)
     x = synthetic.activations(M, K, seed=41)
-    say("prefill crafted scales")
-    y64, absy = oracle_qmm(orc, x, w)
+    # the first rows hold the zero, subnormal and huge scales
+    rows = np.union1d(np.arange(8), np.arange(0, N, max(1, N // 400))).astype(np.int32)
+    say(f"prefill crafted scales M={M} N={N} K={K}")
+    y64, absy = oracle_qmm(orc, x, w, rows=rows)
     y32 = run_prefill(DevWeights(w), x, N, f32=True)
-    check_f32(y32, y64, absy, "prefill crafted")
+    check_f32(y32[:, rows], y64, absy, "prefill crafted")

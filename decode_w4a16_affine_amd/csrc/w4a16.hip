@@ -740,11 +740,14 @@ w4a16_status_t w4a16_matmul_prefill(const uint16_t* x, const uint32_t* qw, const
   if (st != W4A16_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const int f32 = out_dtype == W4A16_OUT_F32;
-  // LDS-tiled form (128 x 128 output tiles) when its grid covers every CU
-  // (measured on MI355X: 256-row tiles of eight waves were 20-50% slower).
+  // LDS-tiled form (128 x 128 output tiles) unless the grid would hold fewer
+  // than 32 tiles; then the per-wave form below splits K inside each block.
+  // Measured on MI355X (us, down projection 2560 <- 10240): M = 512 per-wave
+  // 269, tiled 237 (80 tiles); M = 1024 700 vs 237 (160 tiles).  256-row tiles
+  // of eight waves were 20-50% slower than 128-row tiles of four.
   constexpr int BM = 128;
   const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + BM - 1) / BM;
-  if (tm * tn >= 256) {
+  if (tm * tn >= 32) {
     if (tm * tn > 0x7FFFFFFFL) return W4A16_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(tm * tn));
     if (group == 128)

@@ -218,10 +218,25 @@ struct WaveRows {
   int slot;       // row group within the wave
 };
 
+// Piece stride (float4 units) of the staged activations of a K-tile of CS
+// chunks.  A thread stages one 16-byte piece of x, i.e. pieces 2q and 2q + 1
+// of a chunk, so a 16-lane LDS write pass covers four chunks times four q;
+// with a stride of CS (a multiple of 16 float4) the four q of a chunk fall on
+// the same banks, a 4-way conflict on every staging write (measured: ~4
+// conflict cycles per LDS instruction in the K-split kernels).  With CS + 2,
+// lane (c, q) lands on bank slot 4q + c (mod 16), all distinct; reads (16
+// consecutive chunks of one piece) stay conflict-free.  Padded for M <= 2
+// only: there it measured 1-4% faster (M = 1 step, gate+up, o, M = 2 step);
+// for M >= 3 the larger tile cost a block per CU in some schedules (gate+up at
+// M = 5 10% slower) and the M = 3 and 5 steps 2% slower.
+template <int CS, int M>
+constexpr int kPieceStride = M <= 2 ? CS + 2 : CS;
+
 // Activations of one K-tile as fp32 in LDS.  Layout (float4 units):
-// xs[(m * 8 + piece) * CS + c] holds k = k0 + 32c + 4 piece .. +3.  Threads past
-// the end repeat the last piece (same value, same address).
-template <int M, int XL, int NT, int CS>
+// xs[(m * 8 + piece) * PS + c] holds k = k0 + 32c + 4 piece .. +3 (PS: the
+// piece stride).  Threads past the end repeat the last piece (same value, same
+// address).
+template <int M, int XL, int NT, int PS>
 __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, float4* xs) {
 #pragma unroll
   for (int m = 0; m < M; ++m)
@@ -231,8 +246,8 @@ __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, f
       const int kk = 8 * i;
       const int c = kk >> 5, piece = (kk >> 2) & 7;
       const uint4 v = xv[m][j];
-      xs[(m * 8 + piece) * CS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-      xs[(m * 8 + piece + 1) * CS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+      xs[(m * 8 + piece) * PS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+      xs[(m * 8 + piece + 1) * PS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
     }
 }
 
@@ -249,6 +264,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
                                           int klen, float4* xs) {
   constexpr int LPR = kRowLanes * KSPLIT;
   constexpr int CS = CPL * LPR;                               // chunks per K-tile
+  constexpr int PS = kPieceStride<CS, M>;
   constexpr int KTILE = CS * 32;                              // codes per K-tile
   constexpr int NT = kBlockThreads<KSPLIT, RS>;
   constexpr int XL = (KTILE / 8 + NT - 1) / NT;                // 16-byte x loads per thread per row
@@ -298,8 +314,8 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 #pragma unroll
   for (int j = 0; j < P0; ++j) load_slot(j);
 
-  // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * CS + c]
-  //    holds k = k0 + 32c + 4 piece .. +3 (CS = chunks per K-tile, a
+  // 3. x -> fp32 in LDS.  Layout (float4 units): xs[(m * 8 + piece) * PS + c]
+  //    holds k = k0 + 32c + 4 piece .. +3 (PS = piece stride, a
   //    compile-time stride, so every read offset is an immediate), and lanes
   //    reading consecutive chunks of one piece touch consecutive 16-byte words.
   __syncthreads();  // every wave is done with the previous contents of xs
@@ -312,8 +328,8 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
       const int kk = 8 * i;
       const int c = kk >> 5, piece = (kk >> 2) & 7;
       const uint4 v = xv[m][j];
-      xs[(m * 8 + piece) * CS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-      xs[(m * 8 + piece + 1) * CS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+      xs[(m * 8 + piece) * PS + c] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+      xs[(m * 8 + piece + 1) * PS + c] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
     }
   __syncthreads();
 
@@ -336,9 +352,9 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
         plain |= needs_plain(s[r]);
       }
       if (__any(plain))
-        chunk_fma<M, R, CS, false>(acc, tl.w[j], s, b, xs + c);
+        chunk_fma<M, R, PS, false>(acc, tl.w[j], s, b, xs + c);
       else
-        chunk_fma<M, R, CS, true>(acc, tl.w[j], s, b, xs + c);
+        chunk_fma<M, R, PS, true>(acc, tl.w[j], s, b, xs + c);
     }
   }
 }
@@ -349,7 +365,7 @@ template <int M, int CPL, int KSPLIT>
 constexpr bool kRolled = KSPLIT == 1 && 2 * M * 8 * CPL * kRowLanes * 16 <= 32768;
 // float4 of LDS a block needs for its activation tiles
 template <int M, int CPL, int KSPLIT>
-constexpr int kXsF4 = M * 8 * CPL * kRowLanes * KSPLIT * (kRolled<M, CPL, KSPLIT> ? 2 : 1);
+constexpr int kXsF4 = M * 8 * kPieceStride<CPL * kRowLanes * KSPLIT, M> * (kRolled<M, CPL, KSPLIT> ? 2 : 1);
 
 // The first `ntiles` (>= 2) full K-tiles of the rows, without a K-split, as one
 // software pipeline: the chunk slots form a single stream across tile
@@ -371,7 +387,8 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
   constexpr int NT = kBlockThreads<1>;
   constexpr int XQ = KTILE / 8;                               // 16-byte x pieces per row per tile
   constexpr int XL = (XQ + NT - 1) / NT;
-  constexpr int XBUF = M * 8 * CS;                            // float4 per activation buffer
+  constexpr int PS = kPieceStride<CS, M>;
+  constexpr int XBUF = M * 8 * PS;                            // float4 per activation buffer
   constexpr int D = DEPTH < CPL ? DEPTH : CPL;
   constexpr int P0 = PRE < D ? PRE : D;
   const int L = w.L;
@@ -413,7 +430,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 #pragma unroll
   for (int j = 0; j < P0; ++j) load(j, false, true);
   __syncthreads();   // the block is done with any earlier contents of xs
-  x_stage_tile<M, XL, NT, CS>(xv, XQ, xs);
+  x_stage_tile<M, XL, NT, PS>(xv, XQ, xs);
   x_issue(1);
   __syncthreads();
 #pragma unroll
@@ -429,7 +446,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
       // are consumed right now when D == CPL: then it goes out afterwards)
       if (j + D < CPL) load(j + D, false, true);
       else if (j + D - CPL < j) load(j + D - CPL, true, more);
-      consume_slot<M, R, CS>(acc, tl, j, xb + L + j * LPR);
+      consume_slot<M, R, PS>(acc, tl, j, xb + L + j * LPR);
       if (j + D >= CPL && j + D - CPL == j) load(j, true, more);
     }
 #pragma unroll
@@ -439,7 +456,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
     }
     // tile t + 1's activations into the other buffer (last read during tile
     // t - 1, which every wave finished before the previous barrier)
-    x_stage_tile<M, XL, NT, CS>(xv, XQ, xs + ((t + 1) & 1) * XBUF);
+    x_stage_tile<M, XL, NT, PS>(xv, XQ, xs + ((t + 1) & 1) * XBUF);
     x_issue(t + 2);
     __syncthreads();
   }

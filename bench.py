@@ -137,10 +137,12 @@ def capture(torch, fn):
     return g
 
 
-def time_graph(torch, g, steps: int, warmup: int, min_warm_s: float = 0.0) -> float:
+def time_graph(torch, g, steps: int, warmup: int, min_warm_s: float = 0.0, per_step: bool = False):
     """Replay `warmup` times, and further until `min_warm_s` seconds of replays
     have run (the GPU's clocks settle only after some tenths of a second of
-    load), then time `steps` replays between two events."""
+    load), then time `steps` replays between two events: the mean ms per
+    replay.  per_step: also an event between consecutive replays, and return
+    (mean, [ms of each replay])."""
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -149,15 +151,25 @@ def time_graph(torch, g, steps: int, warmup: int, min_warm_s: float = 0.0) -> fl
         for _ in range(8):
             g.replay()
         torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     # graph replays run on the current stream, where the events are recorded
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
+    ev[0].record()
+    for i in range(steps):
         g.replay()
-    e1.record()
+        if per_step:
+            ev[i + 1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    mean = ev[0].elapsed_time(ev[-1]) / steps
+    if not per_step:
+        return mean
+    return mean, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def percentiles(ms):
+    """p10, median and p90 of per-step times (ms)."""
+    q = np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])
+    return dict(p10=round(float(q[0]), 5), p50=round(float(q[1]), 5), p90=round(float(q[2]), 5))
 
 
 def kernel_durations(torch, w4, stack, layers: int, reps: int = 10):
@@ -353,6 +365,34 @@ def cpu_baseline(host0, seconds: float = 10.0):
                        f"({calls // 6} layer passes, {dt:.1f} s, 1 thread, fp64 accumulation)")
 
 
+def cpu_baseline_threads(host0, threads: int, seconds: float = 10.0):
+    """The same oracle function over row slices of each projection on `threads`
+    host threads (the C call releases the GIL; row results are unchanged)."""
+    import concurrent.futures as cf
+
+    import oracle
+
+    xs = {p: synthetic.activations(1, host0[p].K, seed=0, tag=(100 + i,))
+          for i, p in enumerate(synthetic.LAYER_ORDER)}
+    slices = {p: np.array_split(np.arange(host0[p].N, dtype=np.int32), threads) for p in synthetic.LAYER_ORDER}
+    done_bytes = 0
+    passes = 0
+    with cf.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        while True:
+            for p in synthetic.LAYER_ORDER:
+                w = host0[p]
+                list(ex.map(lambda r: oracle.qmm(xs[p], w.qw, w.scales, w.biases, rows=r), slices[p]))
+                done_bytes += call_bytes(1, w.N, w.K)
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return dict(value=round(done_bytes / dt / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{passes} passes over one layer's q,k,v,o,gate_up,down weights at M=1, rows split "
+                       f"over {threads} threads ({dt:.1f} s, fp64 accumulation)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,9 +437,10 @@ def main():
         g = capture(torch, make_step(w4, stack, M, L))
         steps = args.steps if M == 1 else max(10, args.steps // 2)
         warm = args.warmup if M == 1 else max(3, args.warmup // 2)
-        ms = time_graph(torch, g, steps, warm, FIRST_WARM_S if M == 1 else WARM_S)
+        ms, each = time_graph(torch, g, steps, warm, FIRST_WARM_S if M == 1 else WARM_S, per_step=True)
         nb = step_bytes(M, L)
-        results[M] = dict(ms=ms, gbs=nb / (ms * 1e-3) / 1e9, bytes=nb, steps=steps, warmup=warm)
+        results[M] = dict(ms=ms, gbs=nb / (ms * 1e-3) / 1e9, bytes=nb, steps=steps, warmup=warm,
+                          pct=percentiles(each))
         log(f"M={M}: {ms:.4f} ms/step, {results[M]['gbs']:.1f} GB/s")
         del g
     g = capture(torch, make_step(w4, stack, 1, L, units=UNITS_SEPARATE))
@@ -456,10 +497,14 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, 1 core)")
         cpu = cpu_baseline(host0, args.cpu_seconds)
+        # the GPU machine's CPU share for one GPU is 16 threads, whatever the host reports
+        threads = max(1, min(16, os.cpu_count() or 1))
+        log(f"cpu baseline (oracle, {threads} threads)")
+        cpu_all = cpu_baseline_threads(host0, threads, args.cpu_seconds)
 
     r1 = results[1]
     line = {
@@ -470,6 +515,7 @@ def main():
         "steps": r1["steps"],
         "warmup": r1["warmup"],
         "ms_per_step": round(r1["ms"], 5),
+        "ms_per_step_pct": r1["pct"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -483,11 +529,12 @@ def main():
                                                   gbs=round(r1["bytes"] / (ms_sep * 1e-3) / 1e9, 2))},
         "verify": {str(M): dict(gbs=round(r["gbs"], 2), ms_per_step=round(r["ms"], 5),
                                 frac_of_peak=round(r["gbs"] / PEAK_GBS, 4),
-                                cost_vs_m1=round(r["ms"] / r1["ms"], 4))
+                                cost_vs_m1=round(r["ms"] / r1["ms"], 4), ms_per_step_pct=r["pct"])
                    for M, r in results.items() if M != 1},
         "roofline": roofline,
         "configs": configs,
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_all,
     }
     print(json.dumps(line), flush=True)
 

@@ -178,22 +178,20 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
 
 
 // ---------------------------------------------------------------------------
-// LDS-tiled form for large M.  A block of 2 * BM / 64 waves owns a BM x 128
-// output tile (BM = 128 or 256) and walks K in steps of 64 codes.  Per step the
-// block stages the activation tile (BM rows x 64 bf16) and the weight tile,
-// dequantized once (128 rows x 64 weights, each split into its bf16 hi and lo
-// parts), in LDS; each wave then multiplies a 64 x 64 piece from LDS (4 x 4
-// fragments of 16 x 16, two K halves, hi and lo: 64 matrix instructions per
-// step).  So every weight is dequantized once per BM activation rows and every
-// activation is fetched once per 128 weight rows.  The next step's global
-// loads are in flight while the current step computes.  LDS rows hold 72 bf16
-// (144 bytes): the 16 lanes of a fragment read rows 144 bytes apart, on
-// distinct banks.
+// LDS-tiled form for large M.  A block of four waves owns a 128 x 128 output
+// tile and walks K in steps of 64 codes.  Per step the block stages the
+// activation tile (128 rows x 64 bf16) and the weight tile, dequantized once
+// (128 rows x 64 weights, each split into its bf16 hi and lo parts), in LDS;
+// each wave then multiplies a 64 x 64 piece from LDS (4 x 4 fragments of
+// 16 x 16, two K halves, hi and lo: 64 matrix instructions per step).  So every
+// weight is dequantized once per 128 activation rows and every activation is
+// fetched once per 128 weight rows.  The next step's global loads are in
+// flight while the current step computes.  LDS rows hold 72 bf16 (144 bytes):
+// the 16 lanes of a fragment read rows 144 bytes apart, on distinct banks.
 // ---------------------------------------------------------------------------
-constexpr int kPfBN = 128, kPfBK = 64;
+constexpr int kPfBM = 128, kPfBN = 128, kPfBK = 64;
 constexpr int kPfStr = kPfBK + 8;   // bf16 per LDS row
-template <int BM>
-constexpr int kPfThreads = 2 * BM;
+constexpr int kPfThreads = 256;
 
 // Block -> output tile.  Workgroups go to the eight XCDs (each with its own
 // L2) in turn, so block b runs on XCD b % 8; giving each XCD a contiguous run
@@ -206,9 +204,9 @@ __device__ __forceinline__ int prefill_tile_of(int b, int nb) {
 
 // One K step's global operands of a thread (kept as separate values: arrays
 // or structs of them were placed in LDS by the compiler): four 16-byte
-// activation pieces, WPT packed weight words (WPT == 2 uses .x, .y), and the
+// activation pieces, four packed weight words (32 codes of one row), and the
 // group's scale and bias bits.
-template <int WPT, int G>
+template <int G>
 __device__ __forceinline__ void pf_load(uint4& a0, uint4& a1, uint4& a2, uint4& a3, uint4& w, uint32_t& s,
                                         uint32_t& b, const uint16_t* x0, const uint16_t* x1, const uint16_t* x2,
                                         const uint16_t* x3, const uint32_t* wq, const uint16_t* ws,
@@ -217,19 +215,13 @@ __device__ __forceinline__ void pf_load(uint4& a0, uint4& a1, uint4& a2, uint4& 
   a1 = *reinterpret_cast<const uint4*>(x1 + k0);
   a2 = *reinterpret_cast<const uint4*>(x2 + k0);
   a3 = *reinterpret_cast<const uint4*>(x3 + k0);
-  if constexpr (WPT == 4) {
-    w = *reinterpret_cast<const uint4*>(wq + (k0 >> 3));
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(wq + (k0 >> 3));
-    w = make_uint4(v.x, v.y, 0u, 0u);
-  }
-  const int g = (k0 + 8 * WPT * bq) / G;
+  w = *reinterpret_cast<const uint4*>(wq + (k0 >> 3));
+  const int g = (k0 + 32 * bq) / G;
   s = ws[g];
   b = wb[g];
 }
 
 // activations and the dequantized hi/lo weights of one step into LDS
-template <int WPT>
 __device__ __forceinline__ void pf_stage(const uint4& a0, const uint4& a1, const uint4& a2, const uint4& a3,
                                          const uint4& w, uint32_t s, uint32_t b, uint16_t* As, uint16_t* Bh,
                                          uint16_t* Bl, int ao0, int ao1, int ao2, int ao3, int boff) {
@@ -240,7 +232,7 @@ __device__ __forceinline__ void pf_stage(const uint4& a0, const uint4& a1, const
   const float sv = bf16_lo(s), bv = bf16_lo(b);
   const bool plain = needs_plain(sv);
 #pragma unroll
-  for (int j = 0; j < WPT; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const uint32_t word = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
     float d[8];
     if (plain)
@@ -279,36 +271,33 @@ __device__ __forceinline__ void pf_compute(f32x4_t (&acc)[4][4], const uint16_t*
   }
 }
 
-template <int BM, int G>
-__global__ __launch_bounds__(kPfThreads<BM>) void qmm_prefill_tiled_kernel(
+template <int G>
+__global__ __launch_bounds__(kPfThreads) void qmm_prefill_tiled_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, void* __restrict__ y, int M, int N, int K, int out_f32, int tiles_n) {
-  constexpr int NT = kPfThreads<BM>;
-  constexpr int WPT = kPfBN * (kPfBK / 8) / NT;   // packed words of the weight tile per thread (4 or 2)
-  constexpr int TPR = (kPfBK / 8) / WPT;          // threads per weight row
-  static_assert(BM == 128 || BM == 256, "block height");
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * kPfStr];
+  constexpr int NT = kPfThreads;
+  static_assert(kPfBN * (kPfBK / 8) == 4 * NT && kPfBM * (kPfBK / 8) == 4 * NT, "four 16-byte pieces per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t As[kPfBM * kPfStr];
   __shared__ __attribute__((aligned(16))) uint16_t Bh[kPfBN * kPfStr];
   __shared__ __attribute__((aligned(16))) uint16_t Bl[kPfBN * kPfStr];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int tile = prefill_tile_of((int)blockIdx.x, (int)gridDim.x);
-  const int m0 = tile / tiles_n * BM, n0 = tile % tiles_n * kPfBN;
+  const int m0 = tile / tiles_n * kPfBM, n0 = tile % tiles_n * kPfBN;
 
   // staging: activation piece p = tid + NT i (row p / 8, 16-byte column p % 8);
-  // weight row tid / TPR, words WPT (tid % TPR) .. +WPT-1 of the step (one
-  // 16- or 8-byte load).  Rows past M or N are clamped (in-bounds loads, never
-  // stored).
+  // weight row tid / 2, words 4 (tid % 2) .. +3 of the step (one 16-byte
+  // load).  Rows past M or N are clamped (in-bounds loads, never stored).
   auto xrow = [&](int i) { return x + (size_t)min(m0 + (tid + NT * i) / 8, M - 1) * K + 8 * (tid % 8); };
   auto aofs = [&](int i) { return (tid + NT * i) / 8 * kPfStr + 8 * (tid % 8); };
   const uint16_t *x0 = xrow(0), *x1 = xrow(1), *x2 = xrow(2), *x3 = xrow(3);
   const int ao0 = aofs(0), ao1 = aofs(1), ao2 = aofs(2), ao3 = aofs(3);
-  const int br = tid / TPR, bq = tid % TPR;
+  const int br = tid >> 1, bq = tid & 1;
   const size_t bn = (size_t)min(n0 + br, N - 1);
-  const uint32_t* wq = qw + bn * (size_t)(K >> 3) + WPT * bq;
+  const uint32_t* wq = qw + bn * (size_t)(K >> 3) + 4 * bq;
   const uint16_t* ws = scales + bn * (size_t)(K / G);
   const uint16_t* wb = biases + bn * (size_t)(K / G);
-  const int boff = br * kPfStr + 8 * WPT * bq;
+  const int boff = br * kPfStr + 32 * bq;
 
   const int wm = wave >> 1, wn = wave & 1;   // this wave's 64 x 64 piece
   const int li = lane & 15, lk = lane >> 4;
@@ -323,12 +312,12 @@ __global__ __launch_bounds__(kPfThreads<BM>) void qmm_prefill_tiled_kernel(
   const int steps = K / kPfBK;
   uint4 a0, a1, a2, a3, w;
   uint32_t s, b;
-  pf_load<WPT, G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
+  pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
   for (int st = 0; st < steps; ++st) {
     __syncthreads();   // every wave is done reading the previous step's tiles
-    pf_stage<WPT>(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
+    pf_stage(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
     __syncthreads();
-    if (st + 1 < steps) pf_load<WPT, G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
+    if (st + 1 < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
     pf_compute(acc, As, Bh, Bl, arow, brow, lk);
   }
 

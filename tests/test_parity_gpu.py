@@ -554,7 +554,7 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
 
 
 # ragged M, N and K, both group sizes, tiles and tails in every dimension.  The
-# LDS-tiled form (128 x 128 tiles) runs where M >= 128 and the grid has >= 32
+# LDS-tiled form (128 x 128 tiles) runs where M >= 128 and the grid has >= 64
 # tiles: 257 x 4097, 520 x 2560, 300 x 12837, 520 x 16390 and 256 x 32768 (a
 # grid permuted across the XCDs); the other shapes run the per-wave form.
 PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 4097, 1024, 64), (64, 128, 64, 64),

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kPfBM = 128, kPfBN = 128, kPfBK = 64;
 constexpr int kPfStr = kPfBK + 8;   // bf16 per LDS row
-constexpr int kPfThreads = 256;
+constexpr int kPfThreads = 256;   // per K group
 
 // Block -> output tile.  Workgroups go to the eight XCDs (each with its own
 // L2) in turn, so block b runs on XCD b % 8; giving each XCD a contiguous run
@@ -271,16 +271,27 @@ __device__ __forceinline__ void pf_compute(f32x4_t (&acc)[4][4], const uint16_t*
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(kPfThreads) void qmm_prefill_tiled_kernel(
+// KS = 2 (grids too small to fill the GPU): the block has two groups of four
+// waves, each walking every other K step with its own LDS tiles; at the end
+// group 1 hands its sums to group 0 through LDS, which adds them (group 0's
+// partial first, then group 1's: a fixed order, so results are deterministic).
+// Both groups execute the same barriers, also when the step count is odd.
+template <int G, int KS>
+__global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, void* __restrict__ y, int M, int N, int K, int out_f32, int tiles_n) {
-  constexpr int NT = kPfThreads;
+  constexpr int NT = kPfThreads;   // threads per K group
+  constexpr int TILE = kPfBM * kPfStr;
+  static_assert(kPfBN == kPfBM, "activation and weight tiles of one size");
   static_assert(kPfBN * (kPfBK / 8) == 4 * NT && kPfBM * (kPfBK / 8) == 4 * NT, "four 16-byte pieces per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t As[kPfBM * kPfStr];
-  __shared__ __attribute__((aligned(16))) uint16_t Bh[kPfBN * kPfStr];
-  __shared__ __attribute__((aligned(16))) uint16_t Bl[kPfBN * kPfStr];
-  const int tid = threadIdx.x;
+  static_assert(KS == 1 || KS == 2, "K groups");
+  static_assert(KS == 1 || 16 * NT * 16 <= 3 * KS * TILE * 2, "group sums fit in the tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * KS * TILE];
+  const int kg = (int)threadIdx.x / NT;   // K group
+  const int tid = (int)threadIdx.x % NT;  // thread within the group
+  uint16_t* As = lds + 3 * kg * TILE;
+  uint16_t* Bh = As + TILE;
+  uint16_t* Bl = Bh + TILE;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int tile = prefill_tile_of((int)blockIdx.x, (int)gridDim.x);
   const int m0 = tile / tiles_n * kPfBM, n0 = tile % tiles_n * kPfBN;
@@ -308,17 +319,47 @@ __global__ __launch_bounds__(kPfThreads) void qmm_prefill_tiled_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // the next step's global loads are in flight while the current one computes
+  // the next step's global loads are in flight while the current one computes;
+  // group kg takes steps kg, kg + KS, ... (its last iterations may be empty)
   const int steps = K / kPfBK;
   uint4 a0, a1, a2, a3, w;
   uint32_t s, b;
-  pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
-  for (int st = 0; st < steps; ++st) {
-    __syncthreads();   // every wave is done reading the previous step's tiles
-    pf_stage(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
+  if constexpr (KS == 1) {
+    pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
+    for (int st = 0; st < steps; ++st) {
+      __syncthreads();   // every wave is done reading the previous step's tiles
+      pf_stage(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
+      __syncthreads();
+      if (st + 1 < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
+      pf_compute(acc, As, Bh, Bl, arow, brow, lk);
+    }
+  } else {
+    const int iters = (steps + KS - 1) / KS;
+    if (kg < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, kg * kPfBK, bq);
+    for (int it = 0; it < iters; ++it) {
+      const int st = it * KS + kg;
+      __syncthreads();   // every wave is done reading the previous step's tiles
+      if (st < steps) pf_stage(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
+      __syncthreads();
+      if (st + KS < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + KS) * kPfBK, bq);
+      if (st < steps) pf_compute(acc, As, Bh, Bl, arow, brow, lk);
+    }
+  }
+  if constexpr (KS == 2) {
+    f32x4_t* part = reinterpret_cast<f32x4_t*>(lds);
+    __syncthreads();   // the tiles are free
+    if (kg == 1) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) part[(t * 4 + u) * NT + tid] = acc[t][u];
+    }
     __syncthreads();
-    if (st + 1 < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
-    pf_compute(acc, As, Bh, Bl, arow, brow, lk);
+    if (kg == 1) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[t][u] += part[(t * 4 + u) * NT + tid];
   }
 
 #pragma unroll

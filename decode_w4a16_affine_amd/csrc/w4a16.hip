@@ -740,22 +740,25 @@ w4a16_status_t w4a16_matmul_prefill(const uint16_t* x, const uint32_t* qw, const
   if (st != W4A16_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const int f32 = out_dtype == W4A16_OUT_F32;
-  // LDS-tiled form (128 x 128 output tiles) unless the grid would hold fewer
-  // than 64 tiles; then the per-wave form below splits K inside each block.
-  // Measured on MI355X (us, down projection 2560 <- 10240): M = 256 per-wave
-  // 181, tiled 236 (40 tiles); M = 512 269 vs 237 (80 tiles); M = 1024 700 vs
-  // 237 (160 tiles).  256-row tiles of eight waves were 20-50% slower than
-  // 128-row tiles of four.
+  // LDS-tiled form (128 x 128 output tiles) for M >= 128: with >= 256 tiles
+  // one group of four waves per tile; with 64..255 tiles (too few blocks for
+  // the CUs) two groups splitting K; fewer tiles take the per-wave form below.
+  // Measured on MI355X (us, down projection 2560 <- 10240; one group / two
+  // groups / per-wave form): M = 256 (40 tiles) 236 / 190 / 181, M = 512 (80)
+  // 237 / 191 / 269, M = 1024 (160) 237 / 192 / 700.  256-row tiles of eight
+  // waves were 20-50% slower than 128-row tiles of four.
   const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM;
   if (M >= kPfBM && tm * tn >= 64) {
     if (tm * tn > 0x7FFFFFFFL) return W4A16_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(tm * tn));
+    const bool split = tm * tn < 256;
+    auto go = [&](auto kernel, int threads) {
+      hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, x, qw, scales, biases, y, M, N, K, f32, (int)tn);
+    };
     if (group == 128)
-      hipLaunchKernelGGL(qmm_prefill_tiled_kernel<128>, grid, dim3(kPfThreads), 0, s, x, qw, scales, biases, y, M,
-                         N, K, f32, (int)tn);
+      split ? go(qmm_prefill_tiled_kernel<128, 2>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<128, 1>, kPfThreads);
     else
-      hipLaunchKernelGGL(qmm_prefill_tiled_kernel<64>, grid, dim3(kPfThreads), 0, s, x, qw, scales, biases, y, M,
-                         N, K, f32, (int)tn);
+      split ? go(qmm_prefill_tiled_kernel<64, 2>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<64, 1>, kPfThreads);
     return launched(hipGetLastError());
   }
   // Tiles of 64 activation rows x 32 weight rows per wave; when fewer than

@@ -554,12 +554,14 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
 
 
 # ragged M, N and K, both group sizes, tiles and tails in every dimension.  The
-# LDS-tiled form (128 x 128 tiles) runs where M >= 128 and the grid has >= 64
-# tiles: 257 x 4097, 520 x 2560, 300 x 12837, 520 x 16390 and 256 x 32768 (a
-# grid permuted across the XCDs); the other shapes run the per-wave form.
+# LDS-tiled form (128 x 128 tiles) runs where M >= 128: with >= 256 tiles one
+# group of waves per tile (300 x 12837, 520 x 16390, and 256 x 32768 whose
+# grid is permuted across the XCDs), with 64..255 tiles two groups splitting
+# K (257 x 4097, 520 x 2560, 300 x 3000 at G = 128, and 200 x 8000 with an
+# odd number of K steps); the other shapes run the per-wave form.
 PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 4097, 1024, 64), (64, 128, 64, 64),
            (70, 513, 1280, 128), (1, 77, 256, 128), (520, 2560, 2560, 64), (300, 12837, 640, 128),
-           (520, 16390, 512, 64), (256, 32768, 256, 64)]
+           (520, 16390, 512, 64), (256, 32768, 256, 64), (300, 3000, 640, 128), (200, 8000, 704, 64)]
 
 
 @pytest.mark.parametrize("M,N,K,G", PREFILL)
@@ -579,10 +581,11 @@ def test_prefill_matches_oracle(orc, M, N, K, G):
     assert np.array_equal(run_prefill(dw, x, N, G, f32=True).view(np.uint32), y32.view(np.uint32))   # deterministic
 
 
-@pytest.mark.parametrize("M,N,K", [(20, 64, 2560), (200, 32768, 256)])
+@pytest.mark.parametrize("M,N,K", [(20, 64, 2560), (200, 32768, 256), (150, 8192, 640)])
 def test_prefill_crafted_scales(orc, M, N, K):
     # signs, zero, subnormal and |s| >= 2^100 scales (the plain dequant path),
-    # in the per-wave (M = 20) and the LDS-tiled (M = 200) forms
+    # in the per-wave (M = 20), LDS-tiled (M = 200) and K-split tiled (M = 150,
+    # 128 tiles) forms
     w = synthetic.quantized_weights(N, K, seed=41)
     w.scales, w.biases = crafted_scales(N, K // 64, seed=41)
     x = synthetic.activations(M, K, seed=41)

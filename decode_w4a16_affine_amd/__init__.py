@@ -25,6 +25,7 @@ OUT_BF16 = 0
 OUT_F32 = 1
 GROUP = 64
 MAX_M = 8
+MAX_PREFILL_M = 65536   # W4A16_MAX_PREFILL_M
 
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN",
           5: "ERR_WORKSPACE", 6: "ERR_HIP"}

@@ -26,6 +26,13 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
 
 
+def test_binding_constants_match_header():
+    text = open(HEADER).read()
+    for name, value in (("W4A16_MAX_M", w4.MAX_M), ("W4A16_MAX_PREFILL_M", w4.MAX_PREFILL_M)):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == value, name
+
+
 @pytest.fixture(scope="module")
 def L():
     return w4.lib()

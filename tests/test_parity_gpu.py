@@ -581,6 +581,22 @@ def test_prefill_matches_oracle(orc, M, N, K, G):
     assert np.array_equal(run_prefill(dw, x, N, G, f32=True).view(np.uint32), y32.view(np.uint32))   # deterministic
 
 
+def test_prefill_maximum_rows(orc):
+    # the largest accepted M (65536 rows: 512 row tiles of one weight tile)
+    M, N, K = w4.MAX_PREFILL_M, 130, 64
+    w = synthetic.quantized_weights(N, K, seed=65)
+    x = synthetic.activations(M, K, seed=65)
+    say(f"prefill M={M} N={N} K={K}")
+    # the oracle takes at most 4096 activation rows per call; rows are independent
+    parts = [oracle_qmm(orc, x[i:i + 4096], w) for i in range(0, M, 4096)]
+    y64 = np.concatenate([p[0] for p in parts], axis=0)
+    absy = np.concatenate([p[1] for p in parts], axis=0)
+    dw = DevWeights(w)
+    y32 = run_prefill(dw, x, N, f32=True)
+    check_f32(y32, y64, absy, f"prefill M={M}")
+    assert np.array_equal(run_prefill(dw, x, N), synthetic.bf16_bits(y32))
+
+
 @pytest.mark.parametrize("M,N,K", [(20, 64, 2560), (200, 32768, 256), (150, 8192, 640)])
 def test_prefill_crafted_scales(orc, M, N, K):
     # signs, zero, subnormal and |s| >= 2^100 scales (the plain dequant path),

@@ -106,9 +106,13 @@ struct RoutedSched<MB, 1, CLS> {
   static constexpr int RS = 1;
 };
 // The LM head keeps one row set per block (its block maximum is taken over
-// the waves that hold finished sums).
+// the waves that hold finished sums).  At M = 3 the vocabulary rows take three
+// rows per lane (measured on 262144 x 2560: 111.1 -> 105.5 us; the same
+// schedule is slower for the square 16384 x 16384 matrix, 53.6 -> 74.3 us at
+// M = 4, so it stays specific to the head).
 template <int M, int KSPLIT, int CLS>
 struct LmSched : Sched<M, KSPLIT, CLS> {
+  static constexpr int R = (M == 3 && KSPLIT == 1 && (CLS & 1)) ? 3 : Sched<M, KSPLIT, CLS>::R;
   static constexpr int RS = 1;
 };
 constexpr int kRoutedPassRows = 2;

@@ -225,12 +225,16 @@ struct WaveRows {
 // the same banks, a 4-way conflict on every staging write (measured: ~4
 // conflict cycles per LDS instruction in the K-split kernels).  With CS + 2,
 // lane (c, q) lands on bank slot 4q + c (mod 16), all distinct; reads (16
-// consecutive chunks of one piece) stay conflict-free.  Padded for M <= 2
-// only: there it measured 1-4% faster (M = 1 step, gate+up, o, M = 2 step);
-// for M >= 3 the larger tile cost a block per CU in some schedules (gate+up at
-// M = 5 10% slower) and the M = 3 and 5 steps 2% slower.
-template <int CS, int M>
-constexpr int kPieceStride = M <= 2 ? CS + 2 : CS;
+// consecutive chunks of one piece) stay conflict-free.  PAD selects the
+// padded stride; the kernels pad for M <= 2 (kPadDefault), where it measured
+// 1-4% faster (M = 1 step, gate+up, o, M = 2 step); for M >= 3 the larger tile
+// cost a block per CU in some schedules (gate+up at M = 5 10% slower) and the
+// M = 3 and 5 steps 2% slower.  The LM head never pads (same-box A/B: M = 1
+// unchanged, M = 3 113 -> 109.5 us unpadded).
+template <int CS, bool PAD>
+constexpr int kPieceStride = PAD ? CS + 2 : CS;
+template <int M>
+constexpr bool kPadDefault = M <= 2;
 
 // Activations of one K-tile as fp32 in LDS.  Layout (float4 units):
 // xs[(m * 8 + piece) * PS + c] holds k = k0 + 32c + 4 piece .. +3 (PS: the
@@ -259,12 +263,12 @@ __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, f
 // skipped.  The staging and chunk body are those of x_stage_tile and
 // consume_slot written out in place (through the helpers the compiler
 // allocated 44-71% more registers for the K-split kernels).
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS, int G>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS, int G, bool PAD>
 __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
                                           int klen, float4* xs) {
   constexpr int LPR = kRowLanes * KSPLIT;
   constexpr int CS = CPL * LPR;                               // chunks per K-tile
-  constexpr int PS = kPieceStride<CS, M>;
+  constexpr int PS = kPieceStride<CS, PAD>;
   constexpr int KTILE = CS * 32;                              // codes per K-tile
   constexpr int NT = kBlockThreads<KSPLIT, RS>;
   constexpr int XL = (KTILE / 8 + NT - 1) / NT;                // 16-byte x loads per thread per row
@@ -364,8 +368,8 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 template <int M, int CPL, int KSPLIT>
 constexpr bool kRolled = KSPLIT == 1 && 2 * M * 8 * CPL * kRowLanes * 16 <= 32768;
 // float4 of LDS a block needs for its activation tiles
-template <int M, int CPL, int KSPLIT>
-constexpr int kXsF4 = M * 8 * kPieceStride<CPL * kRowLanes * KSPLIT, M> * (kRolled<M, CPL, KSPLIT> ? 2 : 1);
+template <int M, int CPL, int KSPLIT, bool PAD = kPadDefault<M>>
+constexpr int kXsF4 = M * 8 * kPieceStride<CPL * kRowLanes * KSPLIT, PAD> * (kRolled<M, CPL, KSPLIT> ? 2 : 1);
 
 // The first `ntiles` (>= 2) full K-tiles of the rows, without a K-split, as one
 // software pipeline: the chunk slots form a single stream across tile
@@ -378,7 +382,7 @@ constexpr int kXsF4 = M * 8 * kPieceStride<CPL * kRowLanes * KSPLIT, M> * (kRoll
 // vmcnt waits stay chunk-exact.  Every lane consumes the same chunks in the same
 // order with the same body as tile_pass: the sums are bitwise those of the
 // tile-by-tile walk.  xs must hold 2 * M * 8 * CPL * 16 float4.
-template <int M, int R, int CPL, int PRE, int DEPTH, int G>
+template <int M, int R, int CPL, int PRE, int DEPTH, int G, bool PAD>
 __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w,
                                              int ntiles, float4* xs) {
   constexpr int LPR = kRowLanes;
@@ -387,7 +391,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
   constexpr int NT = kBlockThreads<1>;
   constexpr int XQ = KTILE / 8;                               // 16-byte x pieces per row per tile
   constexpr int XL = (XQ + NT - 1) / NT;
-  constexpr int PS = kPieceStride<CS, M>;
+  constexpr int PS = kPieceStride<CS, PAD>;
   constexpr int XBUF = M * 8 * PS;                            // float4 per activation buffer
   constexpr int D = DEPTH < CPL ? DEPTH : CPL;
   constexpr int P0 = PRE < D ? PRE : D;
@@ -475,8 +479,8 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 // KSPLIT == 1: on return every lane of the row group holds the sums.
 // KSPLIT == S > 1: the S waves of a row set share its rows; on return every
 //              lane of those waves holds the sums (combined in wave order).
-// xs must hold kXsF4<M, CPL, KSPLIT> float4.  Call with all threads (barriers).
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS = 1, int G = 64>
+// xs must hold kXsF4<M, CPL, KSPLIT, PAD> float4.  Call with all threads (barriers).
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS = 1, int G = 64, bool PAD = kPadDefault<M>>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -509,16 +513,16 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   if constexpr (kRolled<M, CPL, KSPLIT>) {
     const int nfull = K / KTILE;
     if (nfull >= 2) {
-      rolled_tiles<M, R, CPL, PRE, DEPTH, G>(acc, xr, w, nfull, xs);
+      rolled_tiles<M, R, CPL, PRE, DEPTH, G, PAD>(acc, xr, w, nfull, xs);
       kr = nfull * KTILE;
     }
   }
   for (int k0 = kr; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
     if (klen == KTILE)
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true, RS, G>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true, RS, G, PAD>(acc, xr, w, k0, klen, xs);
     else
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false, RS, G>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false, RS, G, PAD>(acc, xr, w, k0, klen, xs);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)

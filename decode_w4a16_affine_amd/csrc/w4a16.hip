@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
                                                               const uint16_t* __restrict__ biases,
                                                               void* __restrict__ logits, int out_f32,
                                                               uint64_t* __restrict__ partial, int N, int K) {
-  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
+  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT, false>];   // unpadded staging (see kPieceStride)
   __shared__ float red[kBlockWaves<KSPLIT> * kSlots * R * M];
   __shared__ uint64_t keys[kBlockWaves<KSPLIT>][M];
   using RM = RowMap<R, KSPLIT>;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
   const int block_row0 = blockIdx.x * RM::kRowsPerBlock;
   const int row_first = RM::first_row(block_row0);
   float acc[R][M];
-  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, 1, G>(acc, xr, src, block_row0, xs, red);
+  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, 1, G, false>(acc, xr, src, block_row0, xs, red);
   if (logits) store_to<M, R, KSPLIT>(acc, row_first, N, logits, yoff, out_f32 != 0);
 
   // Block maximum of the (value, index) keys: every lane of a row group holds

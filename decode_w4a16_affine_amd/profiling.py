@@ -8,6 +8,7 @@ the same counter (the benchmark's ``--calibrate-copy`` phase runs one).
 
     python -m decode_w4a16_affine_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
     python -m decode_w4a16_affine_amd.profiling traffic <fetch.csv> <write.csv> <out.json> "<fetch cmd>" "<write cmd>"
+    python -m decode_w4a16_affine_amd.profiling sq <counter_collection.csv> <out.md> "<command>"
 """
 from __future__ import annotations
 
@@ -115,9 +116,35 @@ def traffic_per_launch(record_path: str, kernel: str, grid_sizes_weights: dict):
     return tot / n if n else None
 
 
+def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
+    """Per kernel and grid size: median shader-sequencer counts per launch and
+    per wave (VALU and LDS instructions, LDS bank-conflict cycles per LDS
+    instruction, wave cycles)."""
+    groups = {}
+    for r in csv.DictReader(open(csv_path)):
+        if "qmm_" not in r["Kernel_Name"]:
+            continue
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+        groups.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# Shader-sequencer counters per launch", "", f"Command: `{command}`", "",
+             "| kernel | grid | waves | VALU instr / wave | LDS instr / wave | LDS conflict cycles / LDS instr | "
+             "wave cycles / wave |", "|---|---|---|---|---|---|---|"]
+    for (k, g), d in sorted(groups.items()):
+        med = {c: statistics.median(v) for c, v in d.items()}
+        waves = med.get("SQ_WAVES", 0.0) or 1.0
+        lds = med.get("SQ_INSTS_LDS", 0.0)
+        lines.append(f"| `{k}` | {g} | {int(waves)} | {med.get('SQ_INSTS_VALU', 0.0) / waves:.0f} | {lds / waves:.0f} | "
+                     f"{med.get('SQ_LDS_BANK_CONFLICT', 0.0) / max(lds, 1.0):.2f} | "
+                     f"{med.get('SQ_WAVE_CYCLES', 0.0) / waves:.0f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "stats":
         summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif len(sys.argv) >= 2 and sys.argv[1] == "sq":
+        summarize_sq(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 2 and sys.argv[1] == "traffic":
         print(json.dumps(summarize_traffic(*sys.argv[2:7]), indent=1))
     else:

@@ -5,7 +5,7 @@
  * the product path never does.  It shares no code, header or constant with
  * the HIP library.
  *
- * What it computes (the benchmark spec letters: N = output rows, K = reduction):
+ * What it computes (N = output rows, K = the reduction length):
  *
  *   y[m,n] = sum_k x[m,k] * w[n,k],   w[n,k] = q[n,k]*scale[n,g] + bias[n,g],
  *   g = floor(k / G)

@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
                                  _i64, _i64, _i64, _f64p, _f64p]
         L.orc_argmax.restype = ctypes.c_int
         L.orc_argmax.argtypes = [_f64p, _i64, _i64p, _f64p]
+        L.orc_geglu.restype = ctypes.c_int
+        L.orc_geglu.argtypes = [_f64p, _f64p, _i64, _f64p]
         _lib = L
     return _lib
 
@@ -206,3 +208,23 @@ def argmax(y) -> tuple[int, float]:
     gap = ctypes.c_double(0.0)
     _check(lib().orc_argmax(_ptr(v, _f64p), v.size, ctypes.byref(best), ctypes.byref(gap)), "argmax")
     return int(best.value), float(gap.value)
+
+
+def geglu_values(gate, up) -> np.ndarray:
+    """h = GELU(gate) * up elementwise in fp64 (exact GELU: g * Phi(g))."""
+    g = _c(np.asarray(gate, dtype=np.float64), np.float64)
+    u = _c(np.broadcast_to(np.asarray(up, dtype=np.float64), g.shape), np.float64)
+    h = np.empty_like(g)
+    _check(lib().orc_geglu(_ptr(g, _f64p), _ptr(u, _f64p), g.size, _ptr(h, _f64p)), "geglu")
+    return h
+
+
+def geglu(x, qw, scales, biases, I: int, group: int = 64, cols=None):
+    """Gated MLP activation on a fused [2I, K] gate+up matrix (gate rows 0..I-1,
+    up rows I..2I-1): h[m, j] = GELU(gate[m, j]) * up[m, j] for j in cols (all
+    I when None).  Returns (h, gate, gate_abs, up, up_abs), each [M, len(cols)]:
+    the fp64 sums of the two products and their sum |x w| error scales."""
+    js = np.arange(I, dtype=np.int32) if cols is None else np.asarray(cols, dtype=np.int32)
+    g, ga = qmm(x, qw, scales, biases, group, rows=js)
+    u, ua = qmm(x, qw, scales, biases, group, rows=js + I)
+    return geglu_values(g, u), g, ga, u, ua

@@ -279,3 +279,22 @@ int orc_argmax(const double *y, int64_t N, int64_t *best, double *gap)
         *gap = (N == 1) ? INFINITY : y[b] - second;
     return ORC_OK;
 }
+
+/*
+ * GeGLU feed-forward activation (Gemma-4 E4B megakernel page, "What it does":
+ * the MLP is GeGLU).  The pages name the activation only, so the definition
+ * taken is the exact one: GELU(g) = g * Phi(g), Phi the standard normal CDF,
+ * Phi(g) = (1 + erf(g / sqrt 2)) / 2, and the gated output h = GELU(gate) * up,
+ * all in fp64.  gate[i], up[i] -> h[i] for i < n.
+ */
+int orc_geglu(const double *gate, const double *up, int64_t n, double *h)
+{
+    if (!gate || !up || !h || n < 0)
+        return ORC_EINVAL;
+    for (int64_t i = 0; i < n; i++) {
+        double g = gate[i];
+        double gelu = 0.5 * g * (1.0 + erf(g / sqrt(2.0)));
+        h[i] = gelu * up[i];
+    }
+    return ORC_OK;
+}

@@ -29,6 +29,9 @@ MUTANTS = [
     ("scale/bias swapped", "return orc_dequant(scales[n * (K / G) + g], biases[n * (K / G) + g], q);",
      "return orc_dequant(biases[n * (K / G) + g], scales[n * (K / G) + g], q);"),
     ("routed expert offset", "const uint32_t *qe = qw + e * N * (K / 8);", "const uint32_t *qe = qw + (E - 1 - e) * N * (K / 8);"),
+    ("GELU by the tanh approximation", "double gelu = 0.5 * g * (1.0 + erf(g / sqrt(2.0)));",
+     "double gelu = 0.5 * g * (1.0 + tanh(sqrt(2.0 / 3.141592653589793) * (g + 0.044715 * g * g * g)));"),
+    ("GELU on the up rows", "h[i] = gelu * up[i];", "h[i] = 0.5 * up[i] * (1.0 + erf(up[i] / sqrt(2.0))) * g;"),
 ]
 
 

@@ -433,3 +433,69 @@ def test_argmax_planted_row_and_duplicates(orc):
     y2, _ = orc.qmm(x, np.delete(qw, 200, 0), np.delete(s, 200, 0), np.delete(b, 200, 0))
     best2, gap2 = orc.argmax(y2[0])
     assert best2 == star and gap2 > 1e-3 * 2 * a[0, star]
+
+
+# ---------------------------------------------------------------------------
+# GeGLU activation (Gemma-4 page: GeGLU MLP; GELU(g) = g * Phi(g), exact form)
+# ---------------------------------------------------------------------------
+
+# standard normal CDF values from published tables (15 significant digits)
+PHI_TABLE = {0.5: 0.691462461274013, 1.0: 0.841344746068543, 2.0: 0.977249868051821,
+             3.0: 0.998650101968370, -1.0: 0.158655253931457, -2.5: 0.00620966532577613}
+
+
+def test_gelu_matches_tabulated_normal_cdf(orc):
+    xs = np.array(sorted(PHI_TABLE), dtype=np.float64)
+    got = orc.geglu_values(xs, 1.0)
+    want = np.array([x * PHI_TABLE[x] for x in xs])
+    assert np.all(np.abs(got - want) <= 1e-14 * np.maximum(1.0, np.abs(want)))
+    assert orc.geglu_values(np.array([0.0]), 5.0)[0] == 0.0
+
+
+def test_gelu_odd_part_is_the_identity(orc):
+    # Phi(x) + Phi(-x) = 1, so GELU(x) - GELU(-x) = x for every x
+    x = np.linspace(-8.0, 8.0, 1601)
+    d = orc.geglu_values(x, 1.0) - orc.geglu_values(-x, 1.0)
+    assert np.all(np.abs(d - x) <= 4e-16 * np.maximum(1.0, np.abs(x)))
+
+
+def simpson_phi(x, n=20000):
+    """Standard normal CDF by composite Simpson integration of the density from
+    -12 (where the mass below is < 1e-32): independent of erf."""
+    t = np.linspace(-12.0, x, n + 1)
+    f = np.exp(-0.5 * t * t) / np.sqrt(2.0 * np.pi)
+    h = (x + 12.0) / n
+    return h / 3.0 * (f[0] + f[-1] + 4.0 * f[1:-1:2].sum() + 2.0 * f[2:-1:2].sum())
+
+
+def test_gelu_against_integrated_normal_density(orc):
+    xs = np.array([-5.0, -2.2, -0.7, -0.01, 0.3, 1.3, 2.9, 6.0])
+    got = orc.geglu_values(xs, 1.0)
+    want = np.array([x * simpson_phi(x) for x in xs])
+    assert np.all(np.abs(got - want) <= 1e-11 * np.maximum(1.0, np.abs(xs)))
+
+
+def test_geglu_gates_the_up_rows(orc):
+    # fused [2I, K] matrix: gate rows of codes 9 and up rows of codes 3 with
+    # s = 1/4, b = -2 (both exact), so gate = 0.25 * sum(x) and up = -1.25 * sum(x);
+    # h = GELU(gate) * up, and swapping the halves changes h
+    I, K, M = 3, 128, 2
+    codes = np.concatenate([np.full((I, K), 9, dtype=np.uint8), np.full((I, K), 3, dtype=np.uint8)])
+    qw = packed(orc, codes)
+    s = ones_bf16((2 * I, K // 64), 0.25)
+    b = ones_bf16((2 * I, K // 64), -2.0)
+    x = synthetic.activations(M, K, seed=21)
+    h, g, _, u, _ = orc.geglu(x, qw, s, b, I)
+    sx = np.array([float(sum(bf16_fraction(int(v)) for v in x[m])) for m in range(M)])
+    assert np.allclose(g, np.repeat((0.25 * sx)[:, None], I, axis=1), rtol=1e-15, atol=0)
+    assert np.allclose(u, np.repeat((-1.25 * sx)[:, None], I, axis=1), rtol=1e-15, atol=0)
+    for m in range(M):
+        gm = 0.25 * sx[m]
+        um = -1.25 * sx[m]
+        want = gm * simpson_phi(gm) * um
+        # the integration is accurate to ~1e-13 in Phi (absolute), so scale by |g u|
+        assert np.all(np.abs(h[m] - want) <= 1e-11 * abs(gm * um))
+    h2 = orc.geglu(x, qw, s, b, I, cols=[2, 0])[0]
+    assert np.array_equal(h2, h[:, [2, 0]])
+    swapped = orc.geglu_values(u, g)
+    assert not np.allclose(swapped, h)

@@ -279,6 +279,26 @@ def config_timings(torch, w4, reps: int = 5):
         del qw, sc, bi
     log(f"group128: {out['group128']}")
 
+    # GeGLU on the fused gate+up matrix (w4a16_matmul_geglu: h = GELU(gate) * up,
+    # [M, I] written) beside the plain product of the same matrix ([M, 2I]
+    # written, no activation): the epilogue's cost over the stream it rides on
+    N, K = synthetic.PROJECTIONS["gate_up"]
+    w = synthetic.quantized_weights(N, K, seed=0, tag=(N, 11))
+    copies = max(3, -(-(512 << 20) // w.nbytes))
+    qw, sc, bi = upload(w, copies)
+    del w
+    out["geglu"] = {}
+    for M in (1, 5):
+        x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(N, 11)).view(np.int16)).view(torch.bfloat16).cuda()
+        h = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        calls = [lambda c=c: w4.w4a16_matmul_geglu(x, qw[c], sc[c], bi[c], h) for c in range(copies)]
+        fused = timed(calls, call_bytes(M, N, K) - M * N)
+        calls = [lambda c=c: w4.w4a16_matmul(x, qw[c], sc[c], bi[c], y) for c in range(copies)]
+        out["geglu"][str(M)] = dict(fused, plain_product_us=timed(calls, call_bytes(M, N, K))["us"])
+    del qw, sc, bi
+    log(f"geglu: {out['geglu']}")
+
     # square qmv / qmm
     t = synthetic.SQUARE
     N, K = t["N"], t["K"]

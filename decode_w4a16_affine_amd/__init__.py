@@ -30,7 +30,7 @@ MAX_PREFILL_M = 65536   # W4A16_MAX_PREFILL_M
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN",
           5: "ERR_WORKSPACE", 6: "ERR_HIP"}
 
-EXPORTS = ("w4a16_matmul", "w4a16_matmul_prefill", "w4a16_matmul_grouped", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
+EXPORTS = ("w4a16_matmul", "w4a16_matmul_geglu", "w4a16_matmul_prefill", "w4a16_matmul_grouped", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
            "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_gather_rows", "w4a16_pack", "w4a16_status_str",
            "w4a16_abi_version", "w4a16_schedule_name")
 
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.w4a16_matmul.restype = _int
         L.w4a16_matmul.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]
+        L.w4a16_matmul_geglu.restype = _int
+        L.w4a16_matmul_geglu.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]
         L.w4a16_matmul_prefill.restype = _int
         L.w4a16_matmul_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]
         L.w4a16_matmul_grouped.restype = _int
@@ -140,6 +142,20 @@ def w4a16_matmul(x, qw, scales, biases, y, group: int = GROUP, stream=None) -> N
     N = qw.shape[0]
     _check(lib().w4a16_matmul(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(y), _out_code(y),
                               M, N, K, group, _stream(stream)), "w4a16_matmul")
+
+
+def w4a16_matmul_geglu(x, qw, scales, biases, h, group: int = GROUP, stream=None) -> None:
+    """h[M,I] = GELU(x . Wg^T) * (x . Wu^T) for a fused gate+up matrix qw [2I, K/8]
+    (gate rows first), exact GELU g * Phi(g)."""
+    _dtype(x, torch.bfloat16, "x"); _dtype(qw, torch.int32, "qw")
+    M, K = x.shape
+    if qw.shape[0] % 2:
+        raise ValueError("a fused gate+up matrix has an even number of rows")
+    I = qw.shape[0] // 2
+    if tuple(h.shape) != (M, I):
+        raise ValueError(f"h must be [{M}, {I}], got {list(h.shape)}")
+    _check(lib().w4a16_matmul_geglu(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(h), _out_code(h),
+                                    M, I, K, group, _stream(stream)), "w4a16_matmul_geglu")
 
 
 def w4a16_matmul_prefill(x, qw, scales, biases, y, group: int = GROUP, stream=None) -> None:

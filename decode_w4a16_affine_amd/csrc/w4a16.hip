@@ -329,6 +329,62 @@ __global__ __launch_bounds__(kFinalThreads) void argmax_finalize_kernel(const ui
   }
 }
 
+// Gated MLP activation (the GeGLU MLP of the Gemma-4 megakernel page, "What it
+// does") on a fused gate+up matrix [2I, K]: gate rows
+// 0..I-1, up rows I..2I-1.  A block's waves 0-1 stream gate rows
+// [j0, j0 + 8R) and waves 2-3 the up rows [I + j0, I + j0 + 8R) with the
+// dense product's per-row body and schedule (up waves see the matrix shifted
+// by I - 8R rows), so both sums are bitwise those of w4a16_matmul on the fused
+// matrix; the up sums reach the gate waves through LDS, which write
+// h = GELU(gate) * up, GELU(g) = g * Phi(g) = 0.5 g (1 + erf(g / sqrt 2)), in
+// fp32, rounded once.  Only for matrices without a K-split (2I > 4096).
+template <int M, int R, int CPL, int PRE, int DEPTH, int G>
+__global__ __launch_bounds__(kBlockThreads<1>) void qmm_geglu_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint32_t* qw, const uint16_t* scales,
+                                                                     const uint16_t* biases, void* h, int I, int K,
+                                                                     int out_f32) {
+  __shared__ float4 xs[kXsF4<M, CPL, 1>];
+  __shared__ float red[kBlockWaves<1> * kSlots * R * M];
+  __shared__ float ups[2 * kSlots * R * M];
+  constexpr int kHalf = 2 * kSlots * R;          // gate (and up) rows per block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane & (kRowLanes - 1), slot = lane / kRowLanes;
+  const int j0 = (int)blockIdx.x * kHalf;
+  XRows<M> xr;
+  size_t hoff[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    xr.p[m] = x + (size_t)m * K;
+    hoff[m] = (size_t)m * I;
+  }
+  const bool up = wave >= 2;
+  const size_t shift = up ? (size_t)(I - kHalf) : 0;
+  const RowSrc src{qw + shift * (size_t)(K >> 3), scales + shift * (size_t)((uint32_t)K / G),
+                   biases + shift * (size_t)((uint32_t)K / G), up ? I + kHalf : I, K};
+  float acc[R][M];
+  block_rows<M, R, CPL, 1, PRE, DEPTH, 1, G>(acc, xr, src, j0, xs, red);
+  if (up && t == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) ups[(((wave - 2) * kSlots + slot) * R + r) * M + m] = acc[r][m];
+  }
+  __syncthreads();
+  if (up) return;
+  constexpr float kRsqrt2 = 0.70710678118654752f;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float g = acc[r][m];
+      const float u = ups[((wave * kSlots + slot) * R + r) * M + m];
+      const float gelu = 0.5f * g * (1.0f + erff(g * kRsqrt2));
+      acc[r][m] = gelu * u;
+    }
+  store_to<M, R, 1>(acc, j0 + (wave * kSlots + slot) * R, I, h, hoff, out_f32 != 0);
+}
+
 // One pass of the routed product: C slots routed to one expert.
 template <int C, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int G>
 __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, int x_per_slot, int top_k,
@@ -556,6 +612,47 @@ hipError_t launch_dense(const uint16_t* x, const MatList& ml, int out_f32, int K
   return launch_dense_list<M, S::R, S::CPL, KSPLIT, S::PRE, S::DEPTH, S::RS, G>(x, ml, out_f32, K, st);
 }
 
+template <int M, int CLS, int G>
+hipError_t launch_geglu(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* h,
+                        int out_f32, int I, int K, hipStream_t st) {
+  using S = Sched<M, 1, CLS>;
+  constexpr int kHalf = 2 * kSlots * S::R;
+  const long blocks = ((long)I + kHalf - 1) / kHalf;
+  if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((qmm_geglu_kernel<M, S::R, S::CPL, S::PRE, S::DEPTH, G>), dim3((unsigned)blocks),
+                     dim3(kBlockThreads<1>), 0, st, x, qw, s, b, h, I, K, out_f32);
+  return hipGetLastError();
+}
+
+// The GeGLU product takes the schedule class of its fused matrix, vocabulary
+// heads' schedules mapped to the plain tall ones (the schedule never changes
+// a row's arithmetic).
+template <int M, int G>
+hipError_t geglu_by_class(int cls, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                          void* h, int out_f32, int I, int K, hipStream_t st) {
+  switch (cls & 6) {
+    case 2: return launch_geglu<M, 2, G>(x, qw, s, b, h, out_f32, I, K, st);
+    case 4: return launch_geglu<M, 4, G>(x, qw, s, b, h, out_f32, I, K, st);
+    case 6: return launch_geglu<M, 6, G>(x, qw, s, b, h, out_f32, I, K, st);
+    default: return launch_geglu<M, 0, G>(x, qw, s, b, h, out_f32, I, K, st);
+  }
+}
+
+template <int G>
+hipError_t geglu_dispatch(int M, int cls, const uint16_t* x, const uint32_t* qw, const uint16_t* s,
+                          const uint16_t* b, void* h, int f32, int I, int K, hipStream_t st) {
+  switch (M) {
+    case 1: return geglu_by_class<1, G>(cls, x, qw, s, b, h, f32, I, K, st);
+    case 2: return geglu_by_class<2, G>(cls, x, qw, s, b, h, f32, I, K, st);
+    case 3: return geglu_by_class<3, G>(cls, x, qw, s, b, h, f32, I, K, st);
+    case 4: return geglu_by_class<4, G>(cls, x, qw, s, b, h, f32, I, K, st);
+    case 5: return geglu_by_class<5, G>(cls, x, qw, s, b, h, f32, I, K, st);
+    case 6: return geglu_by_class<6, G>(cls, x, qw, s, b, h, f32, I, K, st);
+    case 7: return geglu_by_class<7, G>(cls, x, qw, s, b, h, f32, I, K, st);
+    default: return geglu_by_class<8, G>(cls, x, qw, s, b, h, f32, I, K, st);
+  }
+}
+
 // Every matrix of `ml` must have the K-split `ksplit`; the schedule class
 // follows the tallest matrix (the class never changes a row's arithmetic).
 template <int M, int G>
@@ -731,6 +828,23 @@ w4a16_status_t w4a16_matmul(const uint16_t* x, const uint32_t* qw, const uint16_
   ml.m[0] = MatDesc{qw, scales, biases, y, N};
   ml.count = 1;
   return launched(dense_dispatch(M, ksplit_for(N, K), x, ml, out_dtype == W4A16_OUT_F32, K, group, (hipStream_t)stream));
+}
+
+w4a16_status_t w4a16_matmul_geglu(const uint16_t* x, const uint32_t* qw, const uint16_t* scales,
+                                  const uint16_t* biases, void* h, int out_dtype, int M, int I, int K, int group,
+                                  void* stream) {
+  if (I < 0 || I > 0x3FFFFFFF) return W4A16_ERR_SHAPE;
+  w4a16_status_t st = check_shape(M, 2 * I, K, group, out_dtype);
+  if (st != W4A16_OK) return st;
+  if (M == 0 || I == 0) return W4A16_OK;
+  if (ksplit_for(2 * I, K) != 1) return W4A16_ERR_UNSUPPORTED;
+  st = check_weights(x, qw, scales, biases, h, out_dtype);
+  if (st != W4A16_OK) return st;
+  const int cls = sched_class(2 * I, K, 1);
+  const int f32 = out_dtype == W4A16_OUT_F32;
+  hipStream_t s = (hipStream_t)stream;
+  return launched(group == 128 ? geglu_dispatch<128>(M, cls, x, qw, scales, biases, h, f32, I, K, s)
+                               : geglu_dispatch<64>(M, cls, x, qw, scales, biases, h, f32, I, K, s));
 }
 
 w4a16_status_t w4a16_matmul_prefill(const uint16_t* x, const uint32_t* qw, const uint16_t* scales,

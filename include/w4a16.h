@@ -88,6 +88,23 @@ w4a16_status_t w4a16_matmul(const uint16_t *x, const uint32_t *qw, const uint16_
                             int group, void *stream);
 
 /*
+ * Gated MLP activation on a fused gate+up matrix (the GeGLU MLP of the
+ * Gemma-4 megakernel page, "What it does"): qw/scales/biases describe a
+ * [2I][K] matrix whose rows 0..I-1 are the gate projection and rows I..2I-1
+ * the up projection (the fused gate_up layout), and
+ *   h[m][j] = GELU(g) * u,  g = (x W^T)[m][j],  u = (x W^T)[m][I + j],
+ * with the exact GELU, GELU(g) = g * Phi(g) (the page names GeGLU but not the
+ * GELU form; the exact one is the reading taken).  g and u are bitwise the
+ * fp32 sums w4a16_matmul produces for those rows of the same matrix; the
+ * activation is computed in fp32 and h rounded once per out_dtype.
+ * h: [M][I].  1 <= M <= 8; needs 2I > 4096 (a matrix the dense product runs
+ * without a K split), else W4A16_ERR_UNSUPPORTED.
+ */
+w4a16_status_t w4a16_matmul_geglu(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
+                                  const uint16_t *biases, void *h, int out_dtype, int M, int I,
+                                  int K, int group, void *stream);
+
+/*
  * Prefill-shaped product, 1 <= M <= W4A16_MAX_PREFILL_M activation rows (a
  * prompt's tokens): the same y = x W^T and dequantization as w4a16_matmul,
  * computed on the matrix cores (tiny-llm page, "Revisit the Decode Roofline":

@@ -1,10 +1,12 @@
 // Prefill-shaped product (M > 8 activation rows) on the gfx950 matrix cores.
 //
-// y[m,n] = sum_k x[m,k] * w[n,k] with w = fma(s, q, b) in fp32, as in the
-// decode kernels.  With many activation rows each weight serves many products,
-// so the work is a dense contraction and runs on v_mfma_f32_16x16x32_bf16:
-// C[16 x 16] += A[16 x 32] * B[32 x 16] with A = x (bf16, exact) and B = w^T.
-// The matrix cores take bf16 operands, so each dequantized fp32 weight is
+// y[m,n] = sum_k x[m,k] * w[n,k], w = s q + b.  With many activation rows each
+// weight serves many products, so the work is a dense contraction and runs on
+// v_mfma_f32_16x16x32_bf16: C[16 x 16] += A[16 x 32] * B[32 x 16] with
+// A = x (bf16, exact).  The LDS-tiled form for large grids (below) multiplies
+// the codes themselves, in the page's rearranged sums.  The per-wave form for
+// small grids uses B = w^T with w = fma(s, q, b) in fp32, as in the decode
+// kernels; the matrix cores take bf16 operands, so each dequantized weight is
 // split into hi = w truncated to bf16 and lo = bf16_rne(w - hi) (w - hi is
 // exact in fp32, below one bf16 ulp of w) and both halves are multiplied:
 // |w - hi - lo| <= 2^-16 |w|, far inside the product's error bound, with fp32
@@ -180,12 +182,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
 // ---------------------------------------------------------------------------
 // LDS-tiled form for large M.  A block of four waves owns a 128 x 128 output
 // tile and walks K in steps of 64 codes.  Per step the block stages the
-// activation tile (128 rows x 64 bf16) and the weight tile, dequantized once
-// (128 rows x 64 weights, each split into its bf16 hi and lo parts), in LDS;
-// each wave then multiplies a 64 x 64 piece from LDS (4 x 4 fragments of
-// 16 x 16, two K halves, hi and lo: 64 matrix instructions per step).  So every
-// weight is dequantized once per 128 activation rows and every activation is
-// fetched once per 128 weight rows.  The next step's global loads are in
+// activation tile (128 rows x 64 bf16), the weight tile as centred codes
+// (128 rows x 64 bf16 integers) and each weight row's scale and shifted bias
+// in LDS; each wave then multiplies a 64 x 64 piece from LDS with the
+// rearranged sums below (4 x 4 fragments of 16 x 16 over two K halves, plus
+// the activation sums of its four row fragments: 40 matrix instructions per
+// step).  So every code is converted once per 128 activation rows and every
+// activation is fetched once per 128 weight rows.  The next step's global loads are in
 // flight while the current step computes.  LDS rows hold 72 bf16 (144 bytes):
 // the 16 lanes of a fragment read rows 144 bytes apart, on distinct banks.
 // ---------------------------------------------------------------------------
@@ -221,52 +224,88 @@ __device__ __forceinline__ void pf_load(uint4& a0, uint4& a1, uint4& a2, uint4& 
   b = wb[g];
 }
 
-// activations and the dequantized hi/lo weights of one step into LDS
-__device__ __forceinline__ void pf_stage(const uint4& a0, const uint4& a1, const uint4& a2, const uint4& a3,
-                                         const uint4& w, uint32_t s, uint32_t b, uint16_t* As, uint16_t* Bh,
-                                         uint16_t* Bl, int ao0, int ao1, int ao2, int ao3, int boff) {
+// ---------------------------------------------------------------------------
+// Rearranged sums (tiny-llm W4 page, "Quantized Matrix Multiplication": the
+// product regrouped per quantization group into a scaled sum of codes plus a
+// bias times the sum of the activations).  With centred codes q' = q - 8 and
+// b' = b + 8 s (so that w = s q' + b'), one K step of 64 codes (inside one
+// group for G = 64 and 128) contributes
+//   y[m, n] += s[n] * P[m, n] + b'[n] * X[m],
+//   P = sum_k x[m, k] q'[n, k],   X = sum_k x[m, k],
+// and q' in [-8, 7] is an exact bf16 integer: one matrix pass over the codes
+// (x q' is exact in fp32) and one against a ones operand for X replace the two
+// passes over split weights.  A row of zero weights stored as q = 8,
+// b = -8 s gives q' = 0 and b' = 0, so exactly 0.  Rounding differs from the
+// literal dequantization: the error is bounded on sum |s x q'| + |b' x|
+// instead of sum |w x| (close for the affine quantizer's b ~ -8 s; a row
+// whose two terms cancel to far below both is the one case that loses
+// relative accuracy).
+// ---------------------------------------------------------------------------
+
+// Eight codes of a packed word as centred bf16 integers q - 8, in code order.
+__device__ __forceinline__ uint4 centred_codes8(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;   // codes 2p / 2p+1 in byte p
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float e = (float)((lo >> (8 * p)) & 0xFFu) - 8.0f;
+    const float d = (float)((hi >> (8 * p)) & 0xFFu) - 8.0f;
+    // small integers: the upper halves of the fp32 values are their exact bf16
+    o[p] = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(e), 0x07060302u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// activations, centred codes and the row's (s, b + 8 s) of one step into LDS
+__device__ __forceinline__ void pf_stage_codes(const uint4& a0, const uint4& a1, const uint4& a2, const uint4& a3,
+                                               const uint4& w, uint32_t s, uint32_t b, uint16_t* As, uint16_t* Bq,
+                                               float2* sb, int ao0, int ao1, int ao2, int ao3, int boff, int br,
+                                               int bq) {
   *reinterpret_cast<uint4*>(As + ao0) = a0;
   *reinterpret_cast<uint4*>(As + ao1) = a1;
   *reinterpret_cast<uint4*>(As + ao2) = a2;
   *reinterpret_cast<uint4*>(As + ao3) = a3;
-  const float sv = bf16_lo(s), bv = bf16_lo(b);
-  const bool plain = needs_plain(sv);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t word = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
-    float d[8];
-    if (plain)
-      dequant8_plain(word, sv, bv, d);
-    else
-      dequant8_fast(word, sv * 0x1p24f, sv * 0x1p20f, bv, d);
-    bf16x8_t hi, lo;
-    split_bf16(d, hi, lo);
-    *reinterpret_cast<bf16x8_t*>(Bh + boff + 8 * j) = hi;
-    *reinterpret_cast<bf16x8_t*>(Bl + boff + 8 * j) = lo;
+  *reinterpret_cast<uint4*>(Bq + boff) = centred_codes8(w.x);
+  *reinterpret_cast<uint4*>(Bq + boff + 8) = centred_codes8(w.y);
+  *reinterpret_cast<uint4*>(Bq + boff + 16) = centred_codes8(w.z);
+  *reinterpret_cast<uint4*>(Bq + boff + 24) = centred_codes8(w.w);
+  if (bq == 0) {
+    const float sv = bf16_lo(s);
+    sb[br] = make_float2(sv, __builtin_fmaf(8.0f, sv, bf16_lo(b)));
   }
 }
 
-// a wave's 64 x 64 piece of one staged step: per K half, its four activation
-// fragments, then per 16-row weight tile the hi and lo fragments (8 matrix
-// instructions each)
-__device__ __forceinline__ void pf_compute(f32x4_t (&acc)[4][4], const uint16_t* As, const uint16_t* Bh,
-                                           const uint16_t* Bl, int arow, int brow, int lk) {
+// a wave's 64 x 64 piece of one staged step: X for its four 16-row activation
+// fragments (ones operand), then per 16-row weight tile P over both K halves
+// and the scaled update of the sums
+__device__ __forceinline__ void pf_compute_codes(f32x4_t (&acc)[4][4], const uint16_t* As, const uint16_t* Bq,
+                                                 const float2* sb, int arow, int brow, int lk) {
+  bf16x8_t a[2][4];
 #pragma unroll
-  for (int ks = 0; ks < kPfBK / 32; ++ks) {
-    bf16x8_t a[4];
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      a[t] = *reinterpret_cast<const bf16x8_t*>(As + (arow + t * 16) * kPfStr + ks * 32 + 8 * lk);
+      a[ks][t] = *reinterpret_cast<const bf16x8_t*>(As + (arow + t * 16) * kPfStr + ks * 32 + 8 * lk);
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4_t X[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int o = (brow + u * 16) * kPfStr + ks * 32 + 8 * lk;
-      const bf16x8_t h = *reinterpret_cast<const bf16x8_t*>(Bh + o);
-      const bf16x8_t l = *reinterpret_cast<const bf16x8_t*>(Bl + o);
+  for (int t = 0; t < 4; ++t) {
+    X[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][t], ones, zero, 0, 0, 0);
+    X[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][t], ones, X[t], 0, 0, 0);
+  }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], h, acc[t][u], 0, 0, 0);
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], l, acc[t][u], 0, 0, 0);
-      }
+  for (int u = 0; u < 4; ++u) {
+    const int o = (brow + u * 16) * kPfStr + 8 * lk;
+    const bf16x8_t q0 = *reinterpret_cast<const bf16x8_t*>(Bq + o);
+    const bf16x8_t q1 = *reinterpret_cast<const bf16x8_t*>(Bq + o + 32);
+    const float2 c = sb[brow + u * 16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][t], q0, zero, 0, 0, 0);
+      P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][t], q1, P, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][u][i] = __builtin_fmaf(c.y, X[t][i], __builtin_fmaf(c.x, P[i], acc[t][u][i]));
     }
   }
 }
@@ -285,13 +324,15 @@ __global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
   static_assert(kPfBN == kPfBM, "activation and weight tiles of one size");
   static_assert(kPfBN * (kPfBK / 8) == 4 * NT && kPfBM * (kPfBK / 8) == 4 * NT, "four 16-byte pieces per thread");
   static_assert(KS == 1 || KS == 2, "K groups");
-  static_assert(KS == 1 || 16 * NT * 16 <= 3 * KS * TILE * 2, "group sums fit in the tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * KS * TILE];
+  // per K group: activation tile, code tile, (s, b') per weight row
+  constexpr int GROUP_LDS = 2 * TILE + 4 * kPfBN;
+  static_assert(KS == 1 || 16 * NT * 16 <= KS * GROUP_LDS * 2, "group sums fit in the tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[KS * GROUP_LDS];
   const int kg = (int)threadIdx.x / NT;   // K group
   const int tid = (int)threadIdx.x % NT;  // thread within the group
-  uint16_t* As = lds + 3 * kg * TILE;
-  uint16_t* Bh = As + TILE;
-  uint16_t* Bl = Bh + TILE;
+  uint16_t* As = lds + kg * GROUP_LDS;
+  uint16_t* Bq = As + TILE;
+  float2* sb = reinterpret_cast<float2*>(Bq + TILE);
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int tile = prefill_tile_of((int)blockIdx.x, (int)gridDim.x);
   const int m0 = tile / tiles_n * kPfBM, n0 = tile % tiles_n * kPfBN;
@@ -328,10 +369,10 @@ __global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
     pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
     for (int st = 0; st < steps; ++st) {
       __syncthreads();   // every wave is done reading the previous step's tiles
-      pf_stage(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
+      pf_stage_codes(a0, a1, a2, a3, w, s, b, As, Bq, sb, ao0, ao1, ao2, ao3, boff, br, bq);
       __syncthreads();
       if (st + 1 < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
-      pf_compute(acc, As, Bh, Bl, arow, brow, lk);
+      pf_compute_codes(acc, As, Bq, sb, arow, brow, lk);
     }
   } else {
     const int iters = (steps + KS - 1) / KS;
@@ -339,10 +380,10 @@ __global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
     for (int it = 0; it < iters; ++it) {
       const int st = it * KS + kg;
       __syncthreads();   // every wave is done reading the previous step's tiles
-      if (st < steps) pf_stage(a0, a1, a2, a3, w, s, b, As, Bh, Bl, ao0, ao1, ao2, ao3, boff);
+      if (st < steps) pf_stage_codes(a0, a1, a2, a3, w, s, b, As, Bq, sb, ao0, ao1, ao2, ao3, boff, br, bq);
       __syncthreads();
       if (st + KS < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + KS) * kPfBK, bq);
-      if (st < steps) pf_compute(acc, As, Bh, Bl, arow, brow, lk);
+      if (st < steps) pf_compute_codes(acc, As, Bq, sb, arow, brow, lk);
     }
   }
   if constexpr (KS == 2) {

@@ -109,9 +109,16 @@ w4a16_status_t w4a16_matmul_geglu(const uint16_t *x, const uint32_t *qw, const u
  * prompt's tokens): the same y = x W^T and dequantization as w4a16_matmul,
  * computed on the matrix cores (tiny-llm page, "Revisit the Decode Roofline":
  * prefill reuses each weight across many rows and needs a matrix schedule).
- * Each fp32 weight fma(s, q, b) enters as bf16 hi + lo parts, so the result
- * stays within the same error bound, but its summation order differs from the
- * M <= 8 schedules: no bitwise equality with w4a16_matmul.  Meant for M > 8.
+ * Large grids (M >= 128 and at least 64 output tiles of 128 x 128) use the
+ * page's rearranged sums ("Quantized Matrix Multiplication"): per 64 codes,
+ * y += s * sum(x * (q - 8)) + (b + 8 s) * sum(x), the centred codes entering
+ * the matrix cores as exact bf16 integers; its rounding is bounded on
+ * sum |s x (q - 8)| + |(b + 8 s) x| rather than sum |w x| (close for
+ * b ~ -8 s; a stored zero weight, q = 8 and b = -8 s, contributes exactly 0).
+ * Smaller grids dequantize each weight with fma(s, q, b) and split it into
+ * bf16 hi + lo parts.  Both orders differ from the M <= 8 schedules: no
+ * bitwise equality with w4a16_matmul.  Deterministic.  Meant for M > 8.
+ * Needs 8 |s| and |s| * 15 finite in fp32.
  */
 w4a16_status_t w4a16_matmul_prefill(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
                                     const uint16_t *biases, void *y, int out_dtype, int M, int N,

@@ -611,3 +611,21 @@ def test_prefill_crafted_scales(orc, M, N, K):
     y64, absy = oracle_qmm(orc, x, w, rows=rows)
     y32 = run_prefill(DevWeights(w), x, N, f32=True)
     check_f32(y32[:, rows], y64, absy, "prefill crafted")
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 1000, 640), (256, 4096, 2560), (1024, 4096, 1280)])
+def test_prefill_zero_weight_rows_exact(orc, M, N, K):
+    # rows stored as q = 8, b = -8 s hold w = 0 exactly, so their outputs are
+    # exactly 0 in the per-wave (M = 100), K-split tiled (64 tiles) and tiled
+    # (256 tiles) forms; the other rows stay within the bound
+    w = synthetic.quantized_weights(N, K, seed=N + 5, bias="exact")
+    zero = np.arange(3, N, 7)
+    w.qw[zero] = 0x88888888
+    x = synthetic.activations(M, K, seed=M + 5)
+    say(f"prefill zero rows M={M} N={N} K={K}")
+    y32 = run_prefill(DevWeights(w), x, N, f32=True)
+    assert np.all(y32[:, zero] == 0), int(np.count_nonzero(y32[:, zero]))
+    rows = np.arange(0, N, max(1, N // 200), dtype=np.int32)
+    y64, absy = oracle_qmm(orc, x, w, rows=rows)
+    assert np.all(y64[:, np.isin(rows, zero)] == 0)
+    check_f32(y32[:, rows], y64, absy, "prefill zero rows")

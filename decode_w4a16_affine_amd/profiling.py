@@ -8,7 +8,12 @@ the same counter (the benchmark's ``--calibrate-copy`` phase runs one).
 
     python -m decode_w4a16_affine_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
     python -m decode_w4a16_affine_amd.profiling traffic <fetch.csv> <write.csv> <out.json> "<fetch cmd>" "<write cmd>"
-    python -m decode_w4a16_affine_amd.profiling sq <counter_collection.csv> <out.md> "<command>"
+    python -m decode_w4a16_affine_amd.profiling sq <counter_collection.csv>[,<more.csv>] <out.md> "<command>"
+    python -m decode_w4a16_affine_amd.profiling prefill-workload
+
+``prefill-workload`` runs the prefill products of the decode stack's gate+up
+and down shapes at M = 4096 (four eager calls each, seeded synthetic inputs):
+the program to run under ``rocprofv3 --pmc`` for the matrix-core kernels.
 """
 from __future__ import annotations
 
@@ -121,27 +126,62 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
     per wave (VALU and LDS instructions, LDS bank-conflict cycles per LDS
     instruction, wave cycles)."""
     groups = {}
-    for r in csv.DictReader(open(csv_path)):
-        if "qmm_" not in r["Kernel_Name"]:
-            continue
-        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
-        groups.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for path in csv_path.split(","):   # several counter passes of the same program
+        for r in csv.DictReader(open(path)):
+            if "qmm_" not in r["Kernel_Name"]:
+                continue
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+            groups.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    matrix = any("SQ_INSTS_MFMA" in d for d in groups.values())
     lines = ["# Shader-sequencer counters per launch", "", f"Command: `{command}`", "",
              "| kernel | grid | waves | VALU instr / wave | LDS instr / wave | LDS conflict cycles / LDS instr | "
-             "wave cycles / wave |", "|---|---|---|---|---|---|---|"]
+             "wave cycles / wave |" + (" MFMA instr / wave | MFMA busy / CU busy (per SIMD) | waiting on a dependency "
+                                       "/ wave cycles | waiting on LDS / wave cycles |" if matrix else ""),
+             "|---|---|---|---|---|---|---|" + ("---|---|---|---|" if matrix else "")]
     for (k, g), d in sorted(groups.items()):
         med = {c: statistics.median(v) for c, v in d.items()}
         waves = med.get("SQ_WAVES", 0.0) or 1.0
         lds = med.get("SQ_INSTS_LDS", 0.0)
-        lines.append(f"| `{k}` | {g} | {int(waves)} | {med.get('SQ_INSTS_VALU', 0.0) / waves:.0f} | {lds / waves:.0f} | "
-                     f"{med.get('SQ_LDS_BANK_CONFLICT', 0.0) / max(lds, 1.0):.2f} | "
-                     f"{med.get('SQ_WAVE_CYCLES', 0.0) / waves:.0f} |")
+        line = (f"| `{k}` | {g} | {int(waves)} | {med.get('SQ_INSTS_VALU', 0.0) / waves:.0f} | {lds / waves:.0f} | "
+                f"{med.get('SQ_LDS_BANK_CONFLICT', 0.0) / max(lds, 1.0):.2f} | "
+                f"{med.get('SQ_WAVE_CYCLES', 0.0) / waves:.0f} |")
+        if matrix:
+            wc = max(med.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+            line += (f" {med.get('SQ_INSTS_MFMA', 0.0) / waves:.0f} | "
+                     f"{med.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / 4 / max(med.get('SQ_BUSY_CU_CYCLES', 0.0), 1.0):.2f} | "
+                     f"{med.get('SQ_WAIT_INST_ANY', 0.0) / wc:.2f} | {med.get('SQ_WAIT_INST_LDS', 0.0) / wc:.2f} |")
+        lines.append(line)
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
+def prefill_workload() -> None:
+    """Four eager prefill calls on each of the gate+up and down shapes at M = 4096."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    import numpy as np
+    import torch
+
+    import decode_w4a16_affine_amd as w4
+    import synthetic
+
+    for name in ("gate_up", "down"):
+        N, K = synthetic.PROJECTIONS[name]
+        w = synthetic.quantized_weights(N, K, seed=0, tag=(N, 7))
+        qw = torch.from_numpy(w.qw.view(np.int32)).cuda()
+        s = torch.from_numpy(w.scales.view(np.int16)).view(torch.bfloat16).cuda()
+        b = torch.from_numpy(w.biases.view(np.int16)).view(torch.bfloat16).cuda()
+        x = torch.from_numpy(synthetic.activations(4096, K, seed=0, tag=(N, 7)).view(np.int16)).view(torch.bfloat16).cuda()
+        y = torch.empty((4096, N), dtype=torch.bfloat16, device="cuda")
+        for _ in range(4):
+            w4.w4a16_matmul_prefill(x, qw, s, b, y)
+        torch.cuda.synchronize()
+        print(f"prefill {name} M=4096: 4 calls", flush=True)
+
+
 if __name__ == "__main__":
-    if len(sys.argv) >= 2 and sys.argv[1] == "stats":
+    if len(sys.argv) >= 2 and sys.argv[1] == "prefill-workload":
+        prefill_workload()
+    elif len(sys.argv) >= 2 and sys.argv[1] == "stats":
         summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 2 and sys.argv[1] == "sq":
         summarize_sq(sys.argv[2], sys.argv[3], sys.argv[4])

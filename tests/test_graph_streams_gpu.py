@@ -2,8 +2,8 @@
 
 The benchmark measures every product through graph replays, and the C ABI is
 stateless (all state lives in caller-owned buffers), so:
-  * a graph holding the dense, grouped, LM-head (logits and argmax), routed and
-    prefill calls reproduces the eager outputs bit for bit on every replay,
+  * a graph holding the dense, grouped, LM-head (logits and argmax), routed,
+    GeGLU and prefill calls reproduces the eager outputs bit for bit on every replay,
     with eager work (clearing the outputs) and synchronizations between the
     replays;
   * the same calls issued on two streams at once, each with its own outputs
@@ -67,10 +67,14 @@ class Calls:
         self.pw = DevWeights(wp)
         self.px = dev_bf16(synthetic.activations(300, K, seed=seed + 40))
         self.py = torch.empty((300, 4096), dtype=torch.bfloat16, device="cuda")
+        wg = synthetic.quantized_weights(2 * 2200, K, seed=seed + 50)
+        self.gw = DevWeights(wg)
+        self.ggx = dev_bf16(synthetic.activations(5, K, seed=seed + 50))
+        self.gh = torch.empty((5, 2200), dtype=torch.bfloat16, device="cuda")
 
     def outputs(self):
         return ([y for (_, _, y) in self.dense.values()] + [y for (_, y) in self.grouped]
-                + [self.logits, self.argmax, self.ey, self.py])
+                + [self.logits, self.argmax, self.ey, self.py, self.gh])
 
     def run(self, stream=None):
         for (w, x, y) in self.dense.values():
@@ -80,6 +84,7 @@ class Calls:
                                stream=stream)
         w4.w4a16_matmul_id(self.ex, self.eq, self.es, self.eb, self.ids, self.ey, stream=stream)
         w4.w4a16_matmul_prefill(self.px, self.pw.qw, self.pw.s, self.pw.b, self.py, stream=stream)
+        w4.w4a16_matmul_geglu(self.ggx, self.gw.qw, self.gw.s, self.gw.b, self.gh, stream=stream)
 
     def snapshot(self):
         torch.cuda.synchronize()

@@ -617,6 +617,8 @@ hipError_t launch_geglu(const uint16_t* x, const uint32_t* qw, const uint16_t* s
                         int out_f32, int I, int K, hipStream_t st) {
   using S = Sched<M, 1, CLS>;
   constexpr int kHalf = 2 * kSlots * S::R;
+  // the up waves view the matrix from row I - kHalf (implied by 2I > 4096)
+  if (I < kHalf) return hipErrorInvalidValue;
   const long blocks = ((long)I + kHalf - 1) / kHalf;
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((qmm_geglu_kernel<M, S::R, S::CPL, S::PRE, S::DEPTH, G>), dim3((unsigned)blocks),

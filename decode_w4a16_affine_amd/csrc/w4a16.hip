@@ -352,12 +352,8 @@ __global__ __launch_bounds__(kBlockThreads<1>) void qmm_geglu_kernel(const uint1
   const int t = lane & (kRowLanes - 1), slot = lane / kRowLanes;
   const int j0 = (int)blockIdx.x * kHalf;
   XRows<M> xr;
-  size_t hoff[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    xr.p[m] = x + (size_t)m * K;
-    hoff[m] = (size_t)m * I;
-  }
+  for (int m = 0; m < M; ++m) xr.p[m] = x + (size_t)m * K;
   const bool up = wave >= 2;
   const size_t shift = up ? (size_t)(I - kHalf) : 0;
   const RowSrc src{qw + shift * (size_t)(K >> 3), scales + shift * (size_t)((uint32_t)K / G),
@@ -372,17 +368,31 @@ __global__ __launch_bounds__(kBlockThreads<1>) void qmm_geglu_kernel(const uint1
   }
   __syncthreads();
   if (up) return;
+  // Lane t of a row group writes the outputs k = r M + m with k % 16 == t
+  // (the dense kernels' store pattern): it picks those gate sums out of its
+  // registers, reads the matching up sums, and evaluates GELU only for them.
   constexpr float kRsqrt2 = 0.70710678118654752f;
+  const int row_first = j0 + (wave * kSlots + slot) * R;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int base = 0; base < R * M; base += kRowLanes) {
+    const int k = base + t;
+    float g = 0.0f;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float g = acc[r][m];
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if (r * M + m == k) g = acc[r][m];
+    const int r = k / M, m = k % M, n = row_first + r;
+    if (k < R * M && n < I) {
       const float u = ups[((wave * kSlots + slot) * R + r) * M + m];
-      const float gelu = 0.5f * g * (1.0f + erff(g * kRsqrt2));
-      acc[r][m] = gelu * u;
+      const float v = 0.5f * g * (1.0f + erff(g * kRsqrt2)) * u;
+      const size_t o = (size_t)m * I + n;
+      if (out_f32)
+        reinterpret_cast<float*>(h)[o] = v;
+      else
+        reinterpret_cast<uint16_t*>(h)[o] = (uint16_t)f32_to_bf16(v);
     }
-  store_to<M, R, 1>(acc, j0 + (wave * kSlots + slot) * R, I, h, hoff, out_f32 != 0);
+  }
 }
 
 // One pass of the routed product: C slots routed to one expert.

@@ -395,6 +395,72 @@ __global__ __launch_bounds__(kBlockThreads<1>) void qmm_geglu_kernel(const uint1
   }
 }
 
+// GeGLU for matrices the dense product splits along K (2I <= 4096): a block of
+// 2 KSPLIT waves holds two row sets of the dense K-split schedule, the gate
+// rows [j0, j0 + 4R) and the up rows [I + j0, I + j0 + 4R) (the up row set
+// views the matrix from row I - 4R, formed in integer arithmetic because it
+// can lie before row 0; only rows from I on are addressed).  Each row set's
+// waves combine their K slices exactly as the dense kernel does, so g and u
+// are again bitwise the dense product's sums; the up sums reach the gate row
+// set through LDS.
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int G>
+__global__ __launch_bounds__((kBlockThreads<KSPLIT, 2>)) void qmm_geglu_split_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, void* h,
+    int I, int K, int out_f32) {
+  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
+  __shared__ float red[kBlockWaves<KSPLIT, 2> * kSlots * R * M];
+  __shared__ float ups[kSlots * R * M];
+  constexpr int kSet = kSlots * R;   // gate (and up) rows per block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane & (kRowLanes - 1), slot = lane / kRowLanes;
+  const int j0 = (int)blockIdx.x * kSet;
+  XRows<M> xr;
+#pragma unroll
+  for (int m = 0; m < M; ++m) xr.p[m] = x + (size_t)m * K;
+  const bool up = wave >= KSPLIT;
+  const intptr_t shift = up ? (intptr_t)I - kSet : 0;   // rows
+  const RowSrc src{reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(qw) +
+                                                     (uintptr_t)(shift * (intptr_t)(K >> 3) * 4)),
+                   reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(scales) +
+                                                     (uintptr_t)(shift * (intptr_t)((uint32_t)K / G) * 2)),
+                   reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(biases) +
+                                                     (uintptr_t)(shift * (intptr_t)((uint32_t)K / G) * 2)),
+                   up ? I + kSet : I, K};
+  float acc[R][M];
+  block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, 2, G>(acc, xr, src, j0, xs, red);
+  if (wave == KSPLIT && t == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) ups[(slot * R + r) * M + m] = acc[r][m];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  constexpr float kRsqrt2 = 0.70710678118654752f;
+  const int row_first = j0 + slot * R;
+#pragma unroll
+  for (int base = 0; base < R * M; base += kRowLanes) {
+    const int k = base + t;
+    float g = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if (r * M + m == k) g = acc[r][m];
+    const int r = k / M, m = k % M, n = row_first + r;
+    if (k < R * M && n < I) {
+      const float u = ups[(slot * R + r) * M + m];
+      const float v = 0.5f * g * (1.0f + erff(g * kRsqrt2)) * u;
+      const size_t o = (size_t)m * I + n;
+      if (out_f32)
+        reinterpret_cast<float*>(h)[o] = v;
+      else
+        reinterpret_cast<uint16_t*>(h)[o] = (uint16_t)f32_to_bf16(v);
+    }
+  }
+}
+
 // One pass of the routed product: C slots routed to one expert.
 template <int C, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int G>
 __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, int x_per_slot, int top_k,
@@ -650,6 +716,32 @@ hipError_t geglu_by_class(int cls, const uint16_t* x, const uint32_t* qw, const 
   }
 }
 
+template <int M, int KS, int CLS, int G>
+hipError_t launch_geglu_split(const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b, void* h,
+                              int out_f32, int I, int K, hipStream_t st) {
+  using S = Sched<M, KS, CLS>;
+  constexpr int kSet = kSlots * S::R;
+  const long blocks = ((long)I + kSet - 1) / kSet;
+  hipLaunchKernelGGL((qmm_geglu_split_kernel<M, S::R, S::CPL, KS, S::PRE, S::DEPTH, G>), dim3((unsigned)blocks),
+                     dim3(kBlockThreads<KS, 2>), 0, st, x, qw, s, b, h, I, K, out_f32);
+  return hipGetLastError();
+}
+
+template <int KS, int CLS, int G>
+hipError_t geglu_split_dispatch(int M, const uint16_t* x, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                                void* h, int f32, int I, int K, hipStream_t st) {
+  switch (M) {
+    case 1: return launch_geglu_split<1, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+    case 2: return launch_geglu_split<2, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+    case 3: return launch_geglu_split<3, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+    case 4: return launch_geglu_split<4, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+    case 5: return launch_geglu_split<5, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+    case 6: return launch_geglu_split<6, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+    case 7: return launch_geglu_split<7, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+    default: return launch_geglu_split<8, KS, CLS, G>(x, qw, s, b, h, f32, I, K, st);
+  }
+}
+
 template <int G>
 hipError_t geglu_dispatch(int M, int cls, const uint16_t* x, const uint32_t* qw, const uint16_t* s,
                           const uint16_t* b, void* h, int f32, int I, int K, hipStream_t st) {
@@ -849,14 +941,24 @@ w4a16_status_t w4a16_matmul_geglu(const uint16_t* x, const uint32_t* qw, const u
   w4a16_status_t st = check_shape(M, 2 * I, K, group, out_dtype);
   if (st != W4A16_OK) return st;
   if (M == 0 || I == 0) return W4A16_OK;
-  if (ksplit_for(2 * I, K) != 1) return W4A16_ERR_UNSUPPORTED;
   st = check_weights(x, qw, scales, biases, h, out_dtype);
   if (st != W4A16_OK) return st;
-  const int cls = sched_class(2 * I, K, 1);
+  const int ks = ksplit_for(2 * I, K);
+  const int cls = sched_class(2 * I, K, ks);
   const int f32 = out_dtype == W4A16_OUT_F32;
   hipStream_t s = (hipStream_t)stream;
-  return launched(group == 128 ? geglu_dispatch<128>(M, cls, x, qw, scales, biases, h, f32, I, K, s)
-                               : geglu_dispatch<64>(M, cls, x, qw, scales, biases, h, f32, I, K, s));
+  if (ks == 1)
+    return launched(group == 128 ? geglu_dispatch<128>(M, cls, x, qw, scales, biases, h, f32, I, K, s)
+                                 : geglu_dispatch<64>(M, cls, x, qw, scales, biases, h, f32, I, K, s));
+  return launched(with_sched(ks, cls, [&](auto k, auto c) -> hipError_t {
+    constexpr int KS = decltype(k)::value, CLS = decltype(c)::value;
+    if constexpr (KS == 1) {
+      return hipErrorInvalidValue;   // handled above
+    } else {
+      return group == 128 ? geglu_split_dispatch<KS, CLS, 128>(M, x, qw, scales, biases, h, f32, I, K, s)
+                          : geglu_split_dispatch<KS, CLS, 64>(M, x, qw, scales, biases, h, f32, I, K, s);
+    }
+  }));
 }
 
 w4a16_status_t w4a16_matmul_prefill(const uint16_t* x, const uint32_t* qw, const uint16_t* scales,

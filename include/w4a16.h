@@ -97,8 +97,7 @@ w4a16_status_t w4a16_matmul(const uint16_t *x, const uint32_t *qw, const uint16_
  * GELU form; the exact one is the reading taken).  g and u are bitwise the
  * fp32 sums w4a16_matmul produces for those rows of the same matrix; the
  * activation is computed in fp32 and h rounded once per out_dtype.
- * h: [M][I].  1 <= M <= 8; needs 2I > 4096 (a matrix the dense product runs
- * without a K split), else W4A16_ERR_UNSUPPORTED.
+ * h: [M][I].  1 <= M <= 8, any I >= 0 (M = 0 or I = 0 writes nothing).
  */
 w4a16_status_t w4a16_matmul_geglu(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
                                   const uint16_t *biases, void *h, int out_dtype, int M, int I,

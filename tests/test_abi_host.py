@@ -95,6 +95,27 @@ def test_prefill_rejects_bad_arguments(L):
     assert pf(x=None, qw=None, y=None, N=0) == OK
 
 
+def test_geglu_rejects_bad_arguments(L):
+    def gg(x=A16, qw=A16, s=A16, h=A16, out=0, M=1, I=3000, K=512, group=64):
+        return L.w4a16_matmul_geglu(x, qw, s, s, h, out, M, I, K, group, None)
+    assert gg(M=9) == EUNSUP
+    assert gg(M=-1) == ESHAPE
+    assert gg(I=-1) == ESHAPE
+    assert gg(I=1 << 30) == ESHAPE           # 2I overflows
+    assert gg(group=32) == EUNSUP
+    assert gg(K=100) == ESHAPE
+    assert gg(out=3) == EUNSUP
+    assert gg(x=None) == ENULL
+    assert gg(h=None) == ENULL
+    assert gg(qw=A4) == EALIGN
+    assert gg(h=A16 + 2, out=1) == EALIGN
+    for I in (1, 2048):                       # the K-split form: the same checks
+        assert gg(I=I, x=None) == ENULL
+        assert gg(I=I, qw=A4) == EALIGN
+    assert gg(x=None, qw=None, s=None, h=None, M=0) == OK
+    assert gg(x=None, qw=None, s=None, h=None, I=0) == OK
+
+
 def test_matmul_empty_problems_launch_nothing(L):
     # empty problems succeed even with NULL pointers: nothing is read or written
     assert mm(L, x=None, qw=None, s=None, b=None, y=None, M=0) == OK

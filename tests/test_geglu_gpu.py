@@ -167,3 +167,21 @@ def test_geglu_rejects_and_empty():
     h0 = torch.full((0, I), 3.0, dtype=torch.bfloat16, device="cuda")
     w4.w4a16_matmul_geglu(torch.zeros((0, K), dtype=torch.bfloat16, device="cuda"), qw, s, s, h0)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("I,K", [(2100, 640), (300, 1024)])
+def test_geglu_crafted_scales(orc, I, K):
+    # signs, zero, subnormal and |s| >= 2^100 scales and biases over a wide
+    # exponent range (the plain dequantization path) in both forms
+    from test_parity_gpu import crafted_scales
+    w = synthetic.quantized_weights(2 * I, K, seed=43)
+    w.scales, w.biases = crafted_scales(2 * I, K // 64, seed=43)
+    # the up rows paired with the first gate rows (which hold the 2^100
+    # scales) get ordinary scales and biases, so g * u stays finite in fp32
+    w.scales[I:I + 8] = synthetic.bf16_bits(np.full((8, K // 64), 0.01, dtype=np.float32))
+    w.biases[I:I + 8] = synthetic.bf16_bits(np.full((8, K // 64), -0.08, dtype=np.float32))
+    x = synthetic.activations(3, K, seed=43)
+    cols = np.arange(I, dtype=np.int32)
+    say(f"geglu crafted scales I={I} K={K}")
+    ref = oracle_geglu(orc, x, w, cols)
+    check(orc, Fused(w), x, cols, ref, f"crafted I={I} K={K}")

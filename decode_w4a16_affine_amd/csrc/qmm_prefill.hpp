@@ -243,13 +243,16 @@ __device__ __forceinline__ void pf_load(uint4& a0, uint4& a1, uint4& a2, uint4& 
 // ---------------------------------------------------------------------------
 
 // Eight codes of a packed word as centred bf16 integers q - 8, in code order.
+// With the top bit of every nibble flipped, a nibble read as a signed 4-bit
+// field is q - 8 (q >= 8: q - 8; q < 8: q + 8 - 16): one signed bitfield
+// extract and one conversion per code.
 __device__ __forceinline__ uint4 centred_codes8(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;   // codes 2p / 2p+1 in byte p
+  const int f = (int)(w ^ 0x88888888u);
   uint32_t o[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float e = (float)((lo >> (8 * p)) & 0xFFu) - 8.0f;
-    const float d = (float)((hi >> (8 * p)) & 0xFFu) - 8.0f;
+    const float e = (float)((int)((uint32_t)f << (28 - 8 * p)) >> 28);   // signed field at bit 8p
+    const float d = (float)((int)((uint32_t)f << (24 - 8 * p)) >> 28);   // signed field at bit 8p + 4
     // small integers: the upper halves of the fp32 values are their exact bf16
     o[p] = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(e), 0x07060302u);
   }

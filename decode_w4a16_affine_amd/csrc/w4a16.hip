@@ -972,15 +972,32 @@ w4a16_status_t w4a16_matmul_prefill(const uint16_t* x, const uint32_t* qw, const
   if (st != W4A16_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const int f32 = out_dtype == W4A16_OUT_F32;
-  // LDS-tiled form (128 x 128 output tiles) for M >= 128: with >= 256 tiles
-  // one group of four waves per tile; with 64..255 tiles (too few blocks for
-  // the CUs) two groups splitting K; fewer tiles take the per-wave form below.
+  // Up to 16 rows: the decode kernels on chunks of at most eight rows, which
+  // stream each weight once per chunk (down 2560 <- 10240, us, per-wave form /
+  // chunks: M = 9 69 / ~30, M = 16 73 / ~48; gate+up M = 9 42 / ~32).
+  if (M <= 2 * W4A16_MAX_M) {
+    const size_t esz = out_dtype == W4A16_OUT_F32 ? 4 : 2;
+    for (int m0 = 0; m0 < M; m0 += W4A16_MAX_M) {
+      const int mc = M - m0 < W4A16_MAX_M ? M - m0 : W4A16_MAX_M;
+      MatList ml{};
+      ml.m[0] = MatDesc{qw, scales, biases, static_cast<char*>(y) + (size_t)m0 * N * esz, N};
+      ml.count = 1;
+      const hipError_t e = dense_dispatch(mc, ksplit_for(N, K), x + (size_t)m0 * K, ml, f32, K, group, s);
+      if (e != hipSuccess) return W4A16_ERR_HIP;
+    }
+    return W4A16_OK;
+  }
+  // LDS-tiled form (128 x 128 output tiles, rows past M clamped) for M >= 32:
+  // with >= 256 tiles one group of four waves per tile; with 64..255 tiles
+  // (too few blocks for the CUs) two groups splitting K; fewer tiles, or
+  // M < 32, take the per-wave form below (gate+up 20480 <- 2560, us, per-wave
+  // / tiled: M = 16 45 / 48, M = 32 52 / 48, M = 64 64 / 48, M = 127 145 / 48).
   // Measured on MI355X (us, down projection 2560 <- 10240; one group / two
   // groups / per-wave form): M = 256 (40 tiles) 236 / 190 / 181, M = 512 (80)
   // 237 / 191 / 269, M = 1024 (160) 237 / 192 / 700.  256-row tiles of eight
   // waves were 20-50% slower than 128-row tiles of four.
   const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM;
-  if (M >= kPfBM && tm * tn >= 64) {
+  if (M >= 32 && tm * tn >= 64) {
     if (tm * tn > 0x7FFFFFFFL) return W4A16_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(tm * tn));
     const bool split = tm * tn < 256;

@@ -108,7 +108,9 @@ w4a16_status_t w4a16_matmul_geglu(const uint16_t *x, const uint32_t *qw, const u
  * prompt's tokens): the same y = x W^T and dequantization as w4a16_matmul,
  * computed on the matrix cores (tiny-llm page, "Revisit the Decode Roofline":
  * prefill reuses each weight across many rows and needs a matrix schedule).
- * Large grids (M >= 128 and at least 64 output tiles of 128 x 128) use the
+ * Up to 16 rows run the decode kernels on chunks of at most 8 rows (each
+ * chunk bitwise equal to a w4a16_matmul call on those rows).  Larger M with
+ * at least 64 output tiles of 128 x 128 (and M >= 32) use the
  * page's rearranged sums ("Quantized Matrix Multiplication"): per 64 codes,
  * y += s * sum(x * (q - 8)) + (b + 8 s) * sum(x), the centred codes entering
  * the matrix cores as exact bf16 integers; its rounding is bounded on

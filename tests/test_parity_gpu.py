@@ -553,15 +553,20 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
     return host_f32(y) if f32 else host_bits(y)
 
 
-# ragged M, N and K, both group sizes, tiles and tails in every dimension.  The
-# LDS-tiled form (128 x 128 tiles) runs where M >= 128: with >= 256 tiles one
-# group of waves per tile (300 x 12837, 520 x 16390, and 256 x 32768 whose
-# grid is permuted across the XCDs), with 64..255 tiles two groups splitting
-# K (257 x 4097, 520 x 2560, 300 x 3000 at G = 128, and 200 x 8000 with an
-# odd number of K steps); the other shapes run the per-wave form.
+# ragged M, N and K, both group sizes, tiles and tails in every dimension.  Up
+# to 16 rows (M = 1, 9 below) run the decode kernels on chunks of eight.  The
+# LDS-tiled form (128 x 128 tiles) runs where M >= 32 and there are >= 64
+# tiles: with >= 256 tiles one group of waves per tile (300 x 12837,
+# 520 x 16390, 256 x 32768 whose grid is permuted across the XCDs, and
+# 100 x 32768 with one partial row tile), with 64..255 tiles two groups
+# splitting K (257 x 4097, 520 x 2560, 300 x 3000 at G = 128, 200 x 8000 with
+# an odd number of K steps, and 40 x 9000 with one partial row tile); the
+# other shapes run the per-wave form (31 x 9000 and 20 x 2560 <- 10240: long
+# K walks with three steps of loads in flight).
 PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 4097, 1024, 64), (64, 128, 64, 64),
            (70, 513, 1280, 128), (1, 77, 256, 128), (520, 2560, 2560, 64), (300, 12837, 640, 128),
-           (520, 16390, 512, 64), (256, 32768, 256, 64), (300, 3000, 640, 128), (200, 8000, 704, 64)]
+           (520, 16390, 512, 64), (256, 32768, 256, 64), (300, 3000, 640, 128), (200, 8000, 704, 64),
+           (40, 9000, 640, 64), (100, 32768, 256, 128), (31, 9000, 2560, 64), (20, 2560, 10240, 64)]
 
 
 @pytest.mark.parametrize("M,N,K,G", PREFILL)
@@ -629,3 +634,19 @@ def test_prefill_zero_weight_rows_exact(orc, M, N, K):
     y64, absy = oracle_qmm(orc, x, w, rows=rows)
     assert np.all(y64[:, np.isin(rows, zero)] == 0)
     check_f32(y32[:, rows], y64, absy, "prefill zero rows")
+
+
+@pytest.mark.parametrize("M,N,K", [(13, 2560, 10240), (16, 20480, 2560), (9, 5000, 640)])
+def test_prefill_small_M_is_the_decode_path(orc, M, N, K):
+    # up to 16 rows the prefill entry runs the decode kernels on chunks of at
+    # most eight rows: bitwise the w4a16_matmul results on those chunks
+    w = synthetic.quantized_weights(N, K, seed=M + N, tag=(3,))
+    x = synthetic.activations(M, K, seed=M + K, tag=(3,))
+    say(f"prefill small M={M} N={N} K={K}")
+    dw = DevWeights(w)
+    y = run_prefill(dw, x, N, f32=True)
+    chunks = np.concatenate([run_mm(dw, x[m0:m0 + 8], N, f32=True) for m0 in range(0, M, 8)])
+    assert np.array_equal(y.view(np.uint32), chunks.view(np.uint32))
+    rows = np.arange(0, N, max(1, N // 200), dtype=np.int32)
+    y64, absy = oracle_qmm(orc, x, w, rows=rows)
+    check_f32(y[:, rows], y64, absy, f"prefill small M={M}")

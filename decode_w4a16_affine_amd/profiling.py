@@ -9,11 +9,12 @@ the same counter (the benchmark's ``--calibrate-copy`` phase runs one).
     python -m decode_w4a16_affine_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
     python -m decode_w4a16_affine_amd.profiling traffic <fetch.csv> <write.csv> <out.json> "<fetch cmd>" "<write cmd>"
     python -m decode_w4a16_affine_amd.profiling sq <counter_collection.csv>[,<more.csv>] <out.md> "<command>"
-    python -m decode_w4a16_affine_amd.profiling prefill-workload
+    python -m decode_w4a16_affine_amd.profiling prefill-workload [M]
 
 ``prefill-workload`` runs the prefill products of the decode stack's gate+up
-and down shapes at M = 4096 (four eager calls each, seeded synthetic inputs):
-the program to run under ``rocprofv3 --pmc`` for the matrix-core kernels.
+and down shapes at M rows (default 4096; four eager calls each, seeded
+synthetic inputs): the program to run under ``rocprofv3 --pmc`` for the
+matrix-core kernels.
 """
 from __future__ import annotations
 
@@ -155,8 +156,8 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
-def prefill_workload() -> None:
-    """Four eager prefill calls on each of the gate+up and down shapes at M = 4096."""
+def prefill_workload(M: int = 4096) -> None:
+    """Four eager prefill calls on each of the gate+up and down shapes at M rows."""
     sys.path.insert(0, os.path.dirname(HERE))
     import numpy as np
     import torch
@@ -170,17 +171,17 @@ def prefill_workload() -> None:
         qw = torch.from_numpy(w.qw.view(np.int32)).cuda()
         s = torch.from_numpy(w.scales.view(np.int16)).view(torch.bfloat16).cuda()
         b = torch.from_numpy(w.biases.view(np.int16)).view(torch.bfloat16).cuda()
-        x = torch.from_numpy(synthetic.activations(4096, K, seed=0, tag=(N, 7)).view(np.int16)).view(torch.bfloat16).cuda()
-        y = torch.empty((4096, N), dtype=torch.bfloat16, device="cuda")
+        x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(N, 7)).view(np.int16)).view(torch.bfloat16).cuda()
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         for _ in range(4):
             w4.w4a16_matmul_prefill(x, qw, s, b, y)
         torch.cuda.synchronize()
-        print(f"prefill {name} M=4096: 4 calls", flush=True)
+        print(f"prefill {name} M={M}: 4 calls", flush=True)
 
 
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "prefill-workload":
-        prefill_workload()
+        prefill_workload(int(sys.argv[2]) if len(sys.argv) >= 3 else 4096)
     elif len(sys.argv) >= 2 and sys.argv[1] == "stats":
         summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 2 and sys.argv[1] == "sq":

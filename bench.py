@@ -35,7 +35,7 @@ import synthetic  # noqa: E402
 METRIC = "achieved HBM GB/s (% of MI355X peak) for W4A16 qmv M=1 and qmm M=k+1"
 PEAK_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
-PREFILL_M = (512, 4096)
+PREFILL_M = (16, 64, 512, 4096)
 LAYERS = 42
 # untimed replay time before each measurement (beyond the warm-up count): the
 # first measurement runs the step for a second so the clocks have settled
@@ -316,24 +316,29 @@ def config_timings(torch, w4, reps: int = 5):
 
     # prefill-sized products (w4a16_matmul_prefill, matrix cores) on the decode
     # stack's gate+up and down shapes: flop-bound, so priced against the dense
-    # bf16 matrix-core peak.  Algorithmic flops are 2*M*N*K.  Both shapes run
-    # the LDS-tiled form at these M, whose matrix cores execute 1.25x that (a
-    # pass over the codes, and a quarter-size pass for the activation sums).
+    # bf16 matrix-core peak.  Algorithmic flops are 2*M*N*K.  From M = 512
+    # both shapes run the LDS-tiled form, whose matrix cores execute 1.25x that
+    # (a pass over the codes, and a quarter-size pass for the activation sums);
+    # M = 16 runs the decode kernels on two 8-row chunks and M = 64 the tiled
+    # form (gate+up) or the per-wave form (down), so for those two the
+    # matrix-core figure is not reported.
     out["prefill"] = {}
     for name in ("gate_up", "down"):
         N, K = synthetic.PROJECTIONS[name]
         w = synthetic.quantized_weights(N, K, seed=0, tag=(N, 7))
-        qw, sc, bi = upload(w, 2)
+        copies = max(2, -(-(512 << 20) // w.nbytes))   # cold weights for the memory-bound small M
+        qw, sc, bi = upload(w, copies)
         del w
         out["prefill"][name] = {}
         for M in PREFILL_M:
             x = torch.from_numpy(synthetic.activations(M, K, seed=0, tag=(N, 7)).view(np.int16)).view(torch.bfloat16).cuda()
             y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-            calls = [lambda c=c: w4.w4a16_matmul_prefill(x, qw[c], sc[c], bi[c], y) for c in (0, 1)]
+            calls = [lambda c=c: w4.w4a16_matmul_prefill(x, qw[c], sc[c], bi[c], y) for c in range(copies)]
             r = timed(calls, call_bytes(M, N, K))
             tflops = 2.0 * M * N * K / (r["us"] * 1e-6) / 1e12
-            r.update(tflops=round(tflops, 1), mfma_tflops=round(1.25 * tflops, 1),
-                     frac_of_bf16_peak=round(tflops / PEAK_BF16_TFLOPS, 4))
+            r.update(tflops=round(tflops, 1), frac_of_bf16_peak=round(tflops / PEAK_BF16_TFLOPS, 4))
+            if M >= 512:
+                r.update(mfma_tflops=round(1.25 * tflops, 1))
             out["prefill"][name][str(M)] = r
             del x, y
         del qw, sc, bi

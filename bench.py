@@ -172,20 +172,67 @@ def percentiles(ms):
     return dict(p10=round(float(q[0]), 5), p50=round(float(q[1]), 5), p90=round(float(q[2]), 5))
 
 
-def kernel_durations(torch, w4, stack, layers: int, reps: int = 10):
-    """Average duration of one launch of each unit of the grouped step: a
-    graph holding that unit's launch for every layer (cold weights) is
-    replayed `reps` times between two events on the replay stream, and the
-    elapsed time is divided by the number of launches.  Graph replays leave no
-    measurable gap between consecutive kernels, so this is the kernel
-    duration."""
+def kernel_durations(torch, w4, stack, layers: int, M: int = 1, reps: int = 10):
+    """Average duration of one launch of each unit of the grouped step at M
+    activation rows: a graph holding that unit's launch for every layer (cold
+    weights) is replayed `reps` times between two events on the replay stream,
+    and the elapsed time is divided by the number of launches.  Graph replays
+    leave no measurable gap between consecutive kernels beyond the launch
+    floor, so this is the kernel duration as the step sees it."""
     out = {}
     for u, ps in UNITS_GROUPED + tuple(x for x in UNITS_SEPARATE if x[0] in ("q", "k", "v")):
         units = UNITS_GROUPED if u in dict(UNITS_GROUPED) else UNITS_SEPARATE
-        g = capture(torch, make_step(w4, stack, 1, layers, units=units, only=(u,)))
+        g = capture(torch, make_step(w4, stack, M, layers, units=units, only=(u,)))
         out[u] = time_graph(torch, g, reps, 2, WARM_S) * 1e3 / layers
         del g
     return out
+
+
+def read_ceiling(torch, nbytes: int = 1 << 30, reps: int = 20):
+    """GB/s of the plain 128-bit streaming-read kernel (libw4a16_probe.so) over
+    `nbytes` of device memory (four times the 256 MB last-level cache), timed
+    launch by launch between events after a second of warm-up."""
+    from decode_w4a16_affine_amd import profiling
+
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    src.fill_(0x01234567)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < FIRST_WARM_S or time.perf_counter() - t0 < 0.2:
+        for _ in range(4):
+            profiling.stream_read(torch, src, sink)
+        torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        profiling.stream_read(torch, src, sink)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del src, sink
+    return dict(gbs=round(float(np.median(gbs)), 1), gbs_best=round(float(gbs.max()), 1),
+                gbs_p10=round(float(np.percentile(gbs, 10)), 1), gbs_p90=round(float(np.percentile(gbs, 90)), 1),
+                frac_of_peak=round(float(np.median(gbs)) / PEAK_GBS, 4), bytes=nbytes, launches=reps,
+                kernel="stream_read_kernel (16-byte loads, 4 in flight per thread, 16 blocks of 256 per CU)")
+
+
+def host_cpu():
+    """CPU model and counts of the host the CPU baseline runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count()
+    return dict(cpu_model=model, nproc=os.cpu_count(), cpus_usable=affinity)
 
 
 def config_timings(torch, w4, reps: int = 5):
@@ -215,12 +262,20 @@ def config_timings(torch, w4, reps: int = 5):
         return qw, sc, bi
 
     def timed(calls, nbytes):
+        # one graph of len(calls) calls over rotated weight copies; every
+        # replay is timed between events, and its mean per call is one sample:
+        # at least 100 calls for calls under 100 MB, at least 20 above
         g = capture(torch, lambda: [c() for c in calls])
-        ms = time_graph(torch, g, reps, 2, WARM_S)
+        need = 100 if nbytes < 100e6 else 20
+        nrep = max(reps, -(-need // len(calls)))
+        _, each = time_graph(torch, g, nrep, 2, WARM_S, per_step=True)
         del g
-        us = ms * 1e3 / len(calls)
+        per_call = np.array(each) * 1e3 / len(calls)
+        p10, us, p90 = (float(v) for v in np.percentile(per_call, [10, 50, 90]))
         gbs = nbytes / (us * 1e-6) / 1e9
-        return dict(us=round(us, 3), gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_GBS, 4))
+        return dict(us=round(us, 3), p10_us=round(p10, 3), p90_us=round(p90, 3),
+                    mean_us=round(float(per_call.mean()), 3), calls=nrep * len(calls),
+                    gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_GBS, 4))
 
     # tiny qmv (latency-bound; reported for completeness)
     t = synthetic.TINY
@@ -512,6 +567,23 @@ def main():
                     per_launch_frac={u: round(unit_bytes(1, unit_ps[u]) / (v * 1e-6) / 1e9 / PEAK_GBS, 4)
                                      for u, v in dur.items()})
 
+    # the verify steps' launches, unit by unit, with the kernel each one runs
+    verify_units = {}
+    for M in results:
+        if M == 1:
+            continue
+        d = kernel_durations(torch, w4, stack, L, M=M)
+        verify_units[M] = {u: dict(us=round(v, 3), gbs=round(unit_bytes(M, unit_ps[u]) / (v * 1e-6) / 1e9, 1),
+                                   frac_of_peak=round(unit_bytes(M, unit_ps[u]) / (v * 1e-6) / 1e9 / PEAK_GBS, 4),
+                                   kernel=w4.w4a16_schedule_name(M, *synthetic.PROJECTIONS[unit_ps[u][0]]))
+                           for u, v in d.items()}
+        log(f"M={M} launches (us): " + ", ".join(f"{u} {v['us']}" for u, v in verify_units[M].items()))
+
+    log("read ceiling (1 GiB, 16-byte streaming read)")
+    ceiling = read_ceiling(torch)
+    log(f"read ceiling: {ceiling['gbs']} GB/s")
+    roofline.update(read_ceiling_gbs=ceiling["gbs"], frac_of_read_ceiling=round(achieved / ceiling["gbs"], 4))
+
     configs = None if args.no_configs else config_timings(torch, w4)
 
     if args.calibrate_copy:
@@ -523,14 +595,18 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    host = host_cpu()
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, 1 core)")
         cpu = cpu_baseline(host0, args.cpu_seconds)
-        # the GPU machine's CPU share for one GPU is 16 threads, whatever the host reports
-        threads = max(1, min(16, os.cpu_count() or 1))
+        # at most 16 threads: the CPU share of one GPU on the benchmark hosts,
+        # whatever the host reports (the host's counts are recorded beside it)
+        threads = max(1, min(16, host["cpus_usable"] or 1))
         log(f"cpu baseline (oracle, {threads} threads)")
         cpu_all = cpu_baseline_threads(host0, threads, args.cpu_seconds)
+        for c in (cpu, cpu_all):
+            c.update(host)
 
     r1 = results[1]
     line = {
@@ -555,9 +631,14 @@ def main():
                                                   gbs=round(r1["bytes"] / (ms_sep * 1e-3) / 1e9, 2))},
         "verify": {str(M): dict(gbs=round(r["gbs"], 2), ms_per_step=round(r["ms"], 5),
                                 frac_of_peak=round(r["gbs"] / PEAK_GBS, 4),
-                                cost_vs_m1=round(r["ms"] / r1["ms"], 4), ms_per_step_pct=r["pct"])
+                                cost_vs_m1=round(r["ms"] / r1["ms"], 4), ms_per_step_pct=r["pct"],
+                                per_launch=verify_units.get(M))
                    for M, r in results.items() if M != 1},
         "roofline": roofline,
+        "read_ceiling": ceiling,
+        "read_ceiling_gbs": ceiling["gbs"],
+        "cpu_model": host["cpu_model"],
+        "host_cpus": host,
         "configs": configs,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_all,

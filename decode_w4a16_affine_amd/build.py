@@ -1,15 +1,23 @@
-"""Compile the HIP library in-tree: decode_w4a16_affine_amd/libw4a16.so (gfx950)."""
+"""Compile the HIP library in-tree: decode_w4a16_affine_amd/libw4a16.so (gfx950).
+
+The decode kernels are instantiated once per activation-row count in separate
+objects (csrc/inst.hip compiled with -DW4K_M=1..8), the prefill kernels and
+the C ABI in two more, all compiled in parallel and linked into one library.
+"""
+import concurrent.futures as cf
 import os
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = [os.path.join(HERE, "csrc", "w4a16.hip")]
+PROBE_LIB = os.path.join(HERE, "libw4a16_probe.so")   # measurement kernels (benchmark only)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # the contract is explicit fma only, never reassociation or contraction
     "-ffp-contract=off", "-fno-fast-math",
     # no packed fp32 arithmetic (v_pk_fma_f32 and friends) in device code
@@ -21,20 +29,62 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# (object name, source, extra defines)
+UNITS = [(f"inst_m{m}", "inst.hip", [f"-DW4K_M={m}"]) for m in range(1, 9)] + [
+    ("prefill", "prefill.hip", []),
+    ("abi", "w4a16.hip", []),
+]
 
-def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, "-o", LIB, *SOURCES]
+_NOISE = "not a recognized feature for this target"
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if _NOISE not in l)
+    return r.returncode, err
+
+
+def build_probe(verbose: bool = False) -> str:
+    """libw4a16_probe.so: the streaming-read kernel the benchmark measures the read ceiling with."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", "-o", tmp, os.path.join(CSRC, "probe.hip")]
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
-    return LIB
+    rc, err = _run(cmd)
+    if rc != 0:
+        raise RuntimeError(f"hipcc failed ({rc}) on probe.hip:\n{err}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
+def build(verbose: bool = False, extra=(), out: str = LIB, jobs: int = None) -> str:
+    jobs = jobs or max(1, min(len(UNITS), os.cpu_count() or 1, 16))
+    with tempfile.TemporaryDirectory(prefix="w4a16_build_") as tmp:
+        cmds = []
+        for name, src, defs in UNITS:
+            obj = os.path.join(tmp, name + ".o")
+            cmds.append((obj, [HIPCC, *FLAGS, *defs, *extra, "-c", "-o", obj, os.path.join(CSRC, src)]))
+        if verbose:
+            for _, c in cmds:
+                print(" ".join(c), flush=True)
+        with cf.ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(lambda oc: _run(oc[1]), cmds))
+        for (obj, c), (rc, err) in zip(cmds, results):
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}) on {os.path.basename(c[-1])} -> {os.path.basename(obj)}:\n{err}")
+            if verbose and err.strip():
+                print(err)
+        tmp_lib = out + ".tmp"
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib, *[o for o, _ in cmds]]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, err = _run(link)
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}):\n{err}")
+        os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)

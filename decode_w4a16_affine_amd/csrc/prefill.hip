@@ -1,0 +1,64 @@
+// Prefill-shaped product above 16 activation rows: the LDS-tiled matrix-core
+// form (qmm_prefill_tiled_kernel) for grids of at least 64 output tiles, the
+// per-wave form (qmm_prefill_kernel) otherwise.  The kernels are in
+// qmm_prefill.hpp; the entry point and the chunked small-M path in w4a16.hip.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ops.hpp"
+#include "qmm_device.hpp"
+#include "qmm_prefill.hpp"
+
+namespace w4k {
+
+hipError_t prefill_large(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
+                         void* y, int f32, int M, int N, int K, int group, hipStream_t s) {
+  // LDS-tiled form (128 x 128 output tiles, rows past M clamped) for M >= 32:
+  // with >= 256 tiles one group of four waves per tile; with 64..255 tiles
+  // (too few blocks for the CUs) two groups splitting K; fewer tiles, or
+  // M < 32, take the per-wave form below (gate+up 20480 <- 2560, us, per-wave
+  // / tiled: M = 16 45 / 48, M = 32 52 / 48, M = 64 64 / 48, M = 127 145 / 48).
+  // Measured on MI355X (us, down projection 2560 <- 10240; one group / two
+  // groups / per-wave form): M = 256 (40 tiles) 236 / 190 / 181, M = 512 (80)
+  // 237 / 191 / 269, M = 1024 (160) 237 / 192 / 700.  256-row tiles of eight
+  // waves were 20-50% slower than 128-row tiles of four.
+  const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM;
+  if (M >= 32 && tm * tn >= 64) {
+    if (tm * tn > 0x7FFFFFFFL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(tm * tn));
+    const bool split = tm * tn < 256;
+    auto go = [&](auto kernel, int threads) {
+      hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, x, qw, scales, biases, y, M, N, K, f32, (int)tn);
+    };
+    if (group == 128)
+      split ? go(qmm_prefill_tiled_kernel<128, 2>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<128, 1>, kPfThreads);
+    else
+      split ? go(qmm_prefill_tiled_kernel<64, 2>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<64, 1>, kPfThreads);
+    return hipGetLastError();
+  }
+  // Tiles of 64 activation rows x 32 weight rows per wave; when fewer than
+  // 1024 such tiles exist, the four waves of a block split K of one tile.
+  constexpr int TM = 4, TN = 2;
+  const long tiles = (long)((M + 16 * TM - 1) / (16 * TM)) * ((N + 16 * TN - 1) / (16 * TN));
+  const bool ksplit = tiles < 1024;
+  const int cols = ksplit ? 16 * TN : kPrefillWaves * 16 * TN;
+  const dim3 grid((unsigned)((N + cols - 1) / cols), (unsigned)((M + 16 * TM - 1) / (16 * TM)));
+  if (group == 128) {
+    if (ksplit)
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 128>), grid, dim3(kPrefillWaves * kWave), 0, s,
+                         x, qw, scales, biases, y, M, N, K, f32);
+    else
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 128>), grid, dim3(kPrefillWaves * kWave), 0, s, x, qw,
+                         scales, biases, y, M, N, K, f32);
+  } else {
+    if (ksplit)
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 64>), grid, dim3(kPrefillWaves * kWave), 0, s,
+                         x, qw, scales, biases, y, M, N, K, f32);
+    else
+      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 64>), grid, dim3(kPrefillWaves * kWave), 0, s, x, qw,
+                         scales, biases, y, M, N, K, f32);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4k

@@ -27,8 +27,35 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(HERE, "csrc", "qmm_device.hpp"), os.path.join(HERE, "csrc", "qmm_prefill.hpp"),
-                  os.path.join(HERE, "csrc", "w4a16.hip")]
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in
+                  ("qmm_device.hpp", "qmm_prefill.hpp", "sched.hpp", "kernels.hpp", "ops.hpp", "inst.hip",
+                   "prefill.hip", "w4a16.hip")]
+PROBE_LIB = os.path.join(HERE, "libw4a16_probe.so")
+
+
+def stream_read(torch, src, sink, blocks: int = 0, stream=None) -> None:
+    """One launch of the 128-bit streaming-read kernel (include/w4a16_probe.h) over
+    the bytes of the contiguous device tensor `src`; `sink` a 4-byte device tensor."""
+    import ctypes
+
+    global _probe
+    try:
+        _probe
+    except NameError:
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is missing: build it with __graft_entry__.build()")
+        _probe = ctypes.CDLL(PROBE_LIB)
+        _probe.w4a16_probe_stream_read.restype = ctypes.c_int
+        _probe.w4a16_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                                   ctypes.c_void_p]
+    if not (src.is_cuda and src.is_contiguous() and sink.is_cuda):
+        raise ValueError("stream_read takes contiguous device tensors")
+    nbytes = src.numel() * src.element_size()
+    st = (stream or torch.cuda.current_stream()).cuda_stream
+    rc = _probe.w4a16_probe_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                        blocks, ctypes.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError(f"w4a16_probe_stream_read failed: hipError {rc}")
 COPY_BYTES = 256 << 20
 
 

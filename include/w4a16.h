@@ -35,12 +35,20 @@
  *     allocates nothing, keeps no state between calls and never synchronizes.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); work
  *     is enqueued on it and the call returns immediately.
- *   - Argument errors are detected before anything is enqueued; on any error
- *     nothing is launched and nothing is written.
+ *   - Argument errors are detected before anything is enqueued; on any such
+ *     error nothing is launched and nothing is written.  W4A16_ERR_HIP (the
+ *     runtime refused a launch) is the exception: entry points that enqueue
+ *     more than one kernel (w4a16_matmul_grouped, w4a16_lmhead_argmax, the
+ *     chunked w4a16_matmul_prefill) may have enqueued the earlier ones, so the
+ *     outputs are then unspecified.
  *   - Calls are re-entrant.  Outputs must not alias inputs.
  *   - Empty problems (M == 0 or N == 0) succeed without launching.
- *   - Alignment: qw and x 16 bytes; scales, biases 2 bytes; y 2 bytes
- *     (bf16) or 4 bytes (fp32); ids, argmax 4 bytes; workspace 8 bytes.
+ *   - Sizes: 0 <= N <= W4A16_MAX_N and K <= W4A16_MAX_K (so that every block
+ *     count and every byte offset inside one wave's rows fits 32 bits);
+ *     larger sizes return W4A16_ERR_SHAPE.
+ *   - Alignment: qw and x 16 bytes (both are read with 16-byte loads);
+ *     scales, biases 2 bytes; y 2 bytes (bf16) or 4 bytes (fp32); ids,
+ *     argmax 4 bytes; workspace 8 bytes.
  *   - 4-bit codes with group == 64 (the workload's) or group == 128 (the
  *     tiny-llm page's); K must be a multiple of the group.
  *   - Asynchronous device faults surface at the caller's next synchronization.
@@ -55,20 +63,27 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 #define W4A16_MAX_M 8
 #define W4A16_MAX_PREFILL_M 65536
 #define W4A16_MAX_GROUP 8
+#define W4A16_MAX_N (1 << 30)
+#define W4A16_MAX_K (1 << 24)
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
     W4A16_ERR_NULL = 1,        /* a required pointer is NULL */
-    W4A16_ERR_SHAPE = 2,       /* a size is negative, K is not a positive multiple of 64,
-                                  top_k/E/R out of range, or a size overflows */
-    W4A16_ERR_UNSUPPORTED = 3, /* group != 64, M > 8, or an unknown out_dtype */
+    W4A16_ERR_SHAPE = 2,       /* a size is negative, K is not a positive multiple of the
+                                  group, N > W4A16_MAX_N, K > W4A16_MAX_K, top_k/E/R or
+                                  a stride out of range */
+    W4A16_ERR_UNSUPPORTED = 3, /* group not 64 or 128, M above the entry point's maximum,
+                                  or an unknown out_dtype */
     W4A16_ERR_ALIGN = 4,       /* a pointer violates the alignment above */
     W4A16_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
-    W4A16_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+    W4A16_ERR_HIP = 6,         /* the HIP runtime rejected a launch */
+    W4A16_STATUS_MAX_ENUM = 0x7FFFFFFF  /* not a status: gives the type the range of a 32-bit
+                                           int, so any value a caller passes back to
+                                           w4a16_status_str is a valid value of it */
 } w4a16_status_t;
 
 typedef enum w4a16_out {
@@ -109,7 +124,8 @@ w4a16_status_t w4a16_matmul_geglu(const uint16_t *x, const uint32_t *qw, const u
  * computed on the matrix cores (tiny-llm page, "Revisit the Decode Roofline":
  * prefill reuses each weight across many rows and needs a matrix schedule).
  * Up to 16 rows run the decode kernels on chunks of at most 8 rows (each
- * chunk bitwise equal to a w4a16_matmul call on those rows).  Larger M with
+ * chunk bitwise equal to a w4a16_matmul call on those rows; a launch error
+ * on the second chunk leaves the first chunk's rows written).  Larger M with
  * at least 64 output tiles of 128 x 128 (and M >= 32) use the
  * page's rearranged sums ("Quantized Matrix Multiplication"): per 64 codes,
  * y += s * sum(x * (q - 8)) + (b + 8 s) * sum(x), the centred codes entering
@@ -117,8 +133,9 @@ w4a16_status_t w4a16_matmul_geglu(const uint16_t *x, const uint32_t *qw, const u
  * sum |s x (q - 8)| + |(b + 8 s) x| rather than sum |w x| (close for
  * b ~ -8 s; a stored zero weight, q = 8 and b = -8 s, contributes exactly 0).
  * Smaller grids dequantize each weight with fma(s, q, b) and split it into
- * bf16 hi + lo parts.  Both orders differ from the M <= 8 schedules: no
- * bitwise equality with w4a16_matmul.  Deterministic.  Meant for M > 8.
+ * bf16 hi + lo parts (bounded on sum |w x| like w4a16_matmul).  Above 16
+ * rows both orders differ from the M <= 8 schedules: no bitwise equality
+ * with w4a16_matmul.  Deterministic.  Meant for M > 8.
  * Needs 8 |s| and |s| * 15 finite in fp32.
  */
 w4a16_status_t w4a16_matmul_prefill(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
@@ -155,15 +172,19 @@ w4a16_status_t w4a16_matmul_grouped(const uint16_t *x, const w4a16_matrix_t *mat
  * (mul_mv_id) of the hy4-preview-metal page's kernel table.
  *   qw [E][N][K/8], scales/biases [E][N][K/64]  (expert e = slab e)
  *   ids int32 [M][top_k], each in [0, E)
- *   x   [M][K] shared by a token's slots (x_per_slot == 0), or
- *       [M][top_k][K] one row per slot (x_per_slot != 0)
- *   y   [M][top_k][N]:  y[m][j][:] = W_{ids[m][j]} . x[m] (or x[m][j])
+ *   x   x_slot_stride == 0: [M][K], row m shared by token m's slots;
+ *       x_slot_stride >= K: one row per slot, slot (m, j) reading the K
+ *       values at x + (m * top_k + j) * x_slot_stride (elements; a multiple
+ *       of 8 so that every row keeps the 16-byte alignment; K gives the dense
+ *       [M][top_k][K] layout)
+ *   y   [M][top_k][N]:  y[m][j][:] = W_{ids[m][j]} . x[m] (or slot (m, j)'s row)
  * Each distinct expert's weights are streamed once for all slots routed to
  * it.  No routing weights are applied.  An id outside [0, E) is a
  * precondition violation: the slot's output row is filled with NaN.
- * 1 <= M <= 8, 1 <= top_k <= 64, 1 <= E.
+ * 1 <= M <= 8, 1 <= top_k <= 64, 1 <= E; any other x_slot_stride (negative,
+ * between 1 and K - 1, not a multiple of 8) returns W4A16_ERR_SHAPE.
  */
-w4a16_status_t w4a16_matmul_id(const uint16_t *x, int x_per_slot, const uint32_t *qw,
+w4a16_status_t w4a16_matmul_id(const uint16_t *x, int64_t x_slot_stride, const uint32_t *qw,
                                const uint16_t *scales, const uint16_t *biases, const int32_t *ids,
                                void *y, int out_dtype, int M, int top_k, int E, int N, int K,
                                int group, void *stream);

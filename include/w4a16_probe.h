@@ -1,0 +1,36 @@
+/*
+ * w4a16_probe.h -- measurement kernels of the W4A16 decode library
+ * (libw4a16_probe.so, gfx950).  Not part of the product: the benchmark uses
+ * them to measure what the hardware gives a plain streaming read, the
+ * ceiling every weight-streaming kernel is judged against beside the 8 TB/s
+ * HBM specification (tiny-llm W4 page, "Revisit the Decode Roofline": decode
+ * time is the streamed bytes over the memory bandwidth).
+ */
+#ifndef W4A16_PROBE_H
+#define W4A16_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Reads `bytes` bytes at `src` (device memory, 16-byte aligned, bytes a
+ * multiple of 16) once with 16-byte loads: each thread keeps four loads in
+ * flight, consecutive lanes read consecutive 16-byte pieces.  The loaded
+ * words are folded into one value per thread, which is stored to sink[0]
+ * only if it equals a constant no input of this benchmark produces (the
+ * store keeps the loads alive and never happens in practice).
+ * blocks: workgroups of 256 threads (0 = 16 per compute unit of device 0).
+ * Returns 0, or a nonzero hipError_t value if the arguments are invalid
+ * (NULL, misaligned, bytes not a multiple of 16) or the launch failed.
+ */
+int w4a16_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_PROBE_H */

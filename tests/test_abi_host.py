@@ -28,9 +28,13 @@ def declared_functions():
 
 def test_binding_constants_match_header():
     text = open(HEADER).read()
-    for name, value in (("W4A16_MAX_M", w4.MAX_M), ("W4A16_MAX_PREFILL_M", w4.MAX_PREFILL_M)):
+    for name, value in (("W4A16_MAX_M", w4.MAX_M), ("W4A16_MAX_PREFILL_M", w4.MAX_PREFILL_M),
+                        ("W4A16_MAX_GROUP", w4.MAX_GROUP)):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m and int(m.group(1)) == value, name
+    for name, value in (("W4A16_MAX_N", w4.MAX_N), ("W4A16_MAX_K", w4.MAX_K)):
+        m = re.search(rf"#define {name} \(1 << (\d+)\)", text)
+        assert m and 1 << int(m.group(1)) == value, name
 
 
 @pytest.fixture(scope="module")
@@ -46,7 +50,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert w4.w4a16_abi_version() == 1
+    assert w4.w4a16_abi_version() == 2
     seen = set()
     for s in range(7):
         txt = w4.w4a16_status_str(s)
@@ -79,6 +83,28 @@ def test_matmul_rejects_bad_arguments(L):
     assert mm(L, x=A4) == EALIGN              # activations are read 16 bytes at a time
     assert mm(L, s=A16 + 1) == EALIGN
     assert mm(L, y=A16 + 2, out=1) == EALIGN  # fp32 output needs 4 bytes
+
+
+def test_sizes_that_would_overflow_block_counts_are_rejected(L):
+    # block counts are (N + rows per block - 1) / rows per block in int, and a
+    # wave's byte offsets are 32-bit: N and K beyond the header's limits fail
+    # validation before any launch
+    big = 2 ** 31 - 1
+    assert mm(L, N=big) == ESHAPE
+    assert mm(L, N=w4.MAX_N + 1) == ESHAPE
+    assert mm(L, N=w4.MAX_N, x=None) == ENULL       # the limit itself passes the size check
+    assert mm(L, K=w4.MAX_K + 64) == ESHAPE
+    assert mm(L, K=w4.MAX_K, x=None) == ENULL
+    assert L.w4a16_lmhead_argmax(A16, A16, A16, A16, None, 0, A16, A16, 1 << 20, 1, big, 512, 64, None) == ESHAPE
+    assert L.w4a16_lmhead_argmax_workspace_bytes(1, big, 512, 64) == 0
+    assert L.w4a16_matmul_prefill(A16, A16, A16, A16, A16, 0, 100, big, 512, 64, None) == ESHAPE
+    assert L.w4a16_matmul_id(A16, 0, A16, A16, A16, A16, A16, 0, 1, 8, 64, big, 512, 64, None) == ESHAPE
+    assert L.w4a16_matmul_geglu(A16, A16, A16, A16, A16, 0, 1, 2 ** 29 + 1, 512, 64, None) == ESHAPE
+    assert L.w4a16_dequant(A16, A16, A16, None, 0, A16, big, 512, 64, None) == ESHAPE
+    assert L.w4a16_gather_rows(A16, A16, A16, A16, 4, A16, big, 512, 64, None) == ESHAPE
+    arr = (w4.Matrix * 1)()
+    arr[0] = w4.Matrix(A16, A16, A16, A16, big)
+    assert L.w4a16_matmul_grouped(A16, arr, 1, 0, 1, 512, 64, None) == ESHAPE
 
 
 def test_prefill_rejects_bad_arguments(L):
@@ -123,8 +149,8 @@ def test_matmul_empty_problems_launch_nothing(L):
 
 
 def test_matmul_id_rejects_bad_arguments(L):
-    def mid(ids=A16, M=1, top_k=8, E=64, N=64, K=128, group=64, x_per_slot=0, out=0):
-        return L.w4a16_matmul_id(A16, x_per_slot, A16, A16, A16, ids, A16, out, M, top_k, E, N, K, group, None)
+    def mid(ids=A16, M=1, top_k=8, E=64, N=64, K=128, group=64, stride=0, out=0):
+        return L.w4a16_matmul_id(A16, stride, A16, A16, A16, ids, A16, out, M, top_k, E, N, K, group, None)
 
     assert mid(group=16) == EUNSUP
     assert mid(M=9) == EUNSUP
@@ -135,6 +161,11 @@ def test_matmul_id_rejects_bad_arguments(L):
     assert mid(ids=None) == ENULL
     assert mid(ids=A16 + 2) == EALIGN
     assert mid(M=0, ids=None) == OK
+    # the per-slot row stride: 0 (shared rows) or >= K and a multiple of 8
+    assert mid(stride=128, ids=None) == ENULL
+    assert mid(stride=136, ids=None) == ENULL
+    for bad in (-128, 8, 120, 130, 2 ** 41):
+        assert mid(stride=bad) == ESHAPE, bad
 
 
 def test_grouped_rejects_bad_arguments(L):
@@ -220,3 +251,64 @@ def test_python_binding_rejects_host_tensors():
         w4.w4a16_matmul(x, qw, s, s, y)
     with pytest.raises(TypeError):
         w4.w4a16_matmul(x.float(), qw, s, s, y)
+
+
+def test_python_binding_checks_shapes_before_the_library():
+    # mis-shaped or mistyped tensors raise before any pointer reaches the
+    # library (CPU tensors: a call that got through would fail on the device
+    # check instead, with a different message)
+    import torch
+
+    bf, i32 = torch.bfloat16, torch.int32
+    x = torch.zeros((2, 128), dtype=bf)
+    qw = torch.zeros((4, 16), dtype=i32)
+    s = torch.zeros((4, 2), dtype=bf)
+    y = torch.zeros((2, 4), dtype=bf)
+
+    def raises(fn, *a, match, **k):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **k)
+
+    raises(w4.w4a16_matmul, x, qw[:, :8], s, s, y, match="qw must have shape")
+    raises(w4.w4a16_matmul, x, qw, s[:, :1], s, y, match="scales must have shape")
+    raises(w4.w4a16_matmul, x, qw, s, s[:3], y, match="biases must have shape")
+    raises(w4.w4a16_matmul, x, qw, s, s, y[:, :3], match="y must have shape")
+    raises(w4.w4a16_matmul, x, qw, s, s, y, group=128, match="scales must have shape")
+    raises(w4.w4a16_matmul, x[0], qw, s, s, y, match="x must be 2-D")
+    raises(w4.w4a16_matmul, x, qw, s, s, y, match="on the GPU")           # shapes fine: device check
+    raises(w4.w4a16_matmul_prefill, x, qw, s, s, y[:1], match="y must have shape")
+    raises(w4.w4a16_matmul_geglu, x, qw, s, s, torch.zeros((2, 4), dtype=bf), match="h must have shape")
+    raises(w4.w4a16_matmul_geglu, x, qw[:3], s[:3], s[:3], torch.zeros((2, 1), dtype=bf), match="even number")
+    raises(w4.w4a16_matmul_grouped, x, [(qw, s, s, y), (qw, s, s, y[:, :2])], match=r"mats\[1\].y")
+    # routed: expert stack, ids and the per-slot activation layout
+    E, top_k = 3, 2
+    eq = torch.zeros((E, 4, 16), dtype=i32)
+    es = torch.zeros((E, 4, 2), dtype=bf)
+    ids = torch.zeros((2, top_k), dtype=i32)
+    yr = torch.zeros((2, top_k, 4), dtype=bf)
+    raises(w4.w4a16_matmul_id, x, eq[:, :, :8], es, es, ids, yr, match="qw must have shape")
+    raises(w4.w4a16_matmul_id, x, eq, es[:2], es, ids, yr, match="scales must have shape")
+    raises(w4.w4a16_matmul_id, x, eq, es, es, ids, yr[:, :1], match="y must have shape")
+    raises(w4.w4a16_matmul_id, x[:1], eq, es, es, ids, yr, match="x must have shape")
+    raises(w4.w4a16_matmul_id, torch.zeros((2, 3, 128), dtype=bf), eq, es, es, ids, yr, match="x must have shape")
+    raises(w4.w4a16_matmul_id, torch.zeros((2, top_k, 256), dtype=bf)[:, :, ::2], eq, es, es, ids, yr,
+           match="unit stride")
+    raises(w4.w4a16_matmul_id, x, eq, es, es, ids[0], yr, match="ids must be 2-D")
+    with pytest.raises(TypeError):
+        w4.w4a16_matmul_id(x, eq, es, es, ids.long(), yr)
+    # LM head, dequant, gather, pack
+    am = torch.zeros((2,), dtype=i32)
+    ws = torch.zeros((64,), dtype=torch.uint8)
+    raises(w4.w4a16_lmhead_argmax, x, qw, s, s, None, am[:1], ws, match="argmax must have shape")
+    raises(w4.w4a16_lmhead_argmax, x, qw, s, s, y[:, :2], am, ws, match="logits must have shape")
+    with pytest.raises(TypeError):
+        w4.w4a16_lmhead_argmax(x, qw, s, s, None, am, ws.float())
+    out = torch.zeros((4, 128), dtype=torch.float32)
+    raises(w4.w4a16_dequant, qw, s, s, out[:3], match="out must have shape")
+    raises(w4.w4a16_dequant, qw, s, s, out[:2], rows=torch.zeros((3,), dtype=i32), match="out must have shape")
+    with pytest.raises(TypeError):
+        w4.w4a16_dequant(qw, s, s, out[:2], rows=torch.zeros((2,), dtype=torch.int64))
+    raises(w4.w4a16_gather_rows, qw, s, s, torch.zeros((2,), dtype=i32), torch.zeros((2, 64), dtype=bf),
+           match="out must have shape")
+    raises(w4.w4a16_pack, torch.zeros((4, 128), dtype=torch.uint8), qw[:, :8], match="qw must have shape")
+    raises(w4.w4a16_pack, torch.zeros((4, 12), dtype=torch.uint8), qw, match="multiple of 8")

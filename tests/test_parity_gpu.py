@@ -200,20 +200,34 @@ def test_long_reduction_segments(orc, M):
         assert np.array_equal(y1[0].view(np.uint32), y32[m].view(np.uint32)), m
 
 
+_SQUARE = {}
+
+
+def square_case(orc):
+    """The 16384 x 16384 workload and the oracle's outputs for all of its rows
+    at the eight activation rows (row m depends on x[m] alone, so the M = 1
+    and 4 calls compare with the first rows)."""
+    if not _SQUARE:
+        N = K = 16384
+        w = synthetic.quantized_weights(N, K, seed=0, tag=(16384,))
+        x = synthetic.activations(8, K, seed=0, tag=(16384,))
+        say(f"square 16384^2: oracle on all {N} rows, M=8 (16 threads)")
+        y64, absy = oracle_qmm(orc, x, w, workers=16)
+        _SQUARE.update(w=w, x=x, y64=y64, absy=absy, dw=DevWeights(w))
+    return _SQUARE
+
+
 @pytest.mark.parametrize("M", synthetic.SQUARE["M"])
 def test_square_16384(orc, M):
     N = K = 16384
-    w = synthetic.quantized_weights(N, K, seed=0, tag=(16384,))
-    x = synthetic.activations(8, K, seed=0, tag=(16384,))
-    rows = np.random.default_rng(1).choice(N, size=384, replace=False).astype(np.int32)
-    rows.sort()
-    say(f"square 16384^2 M={M}: oracle on {len(rows)} rows")
-    y64, absy = oracle_qmm(orc, x[:M], w, rows=rows)
-    dw = DevWeights(w)
+    c = square_case(orc)
+    x, dw = c["x"], c["dw"]
+    y64, absy = c["y64"][:M], c["absy"][:M]
+    say(f"square 16384^2 M={M}: every output against the oracle")
     y32 = run_mm(dw, x[:M], N, f32=True)
-    check_f32(y32[:, rows], y64, absy, f"square M={M}")
+    check_f32(y32, y64, absy, f"square M={M}")
     yb = run_mm(dw, x[:M], N)
-    check_bf16(orc, yb[:, rows], y64, absy, K, f"square M={M}")
+    check_bf16(orc, yb, y64, absy, K, f"square M={M}")
     assert np.array_equal(yb, synthetic.bf16_bits(y32))
     if M > 1:
         for m in range(M):
@@ -349,11 +363,51 @@ def test_lmhead_argmax_config(orc):
             assert am[m] == int(np.flatnonzero(y32[m] == y32[m].max())[0])
         n = check_argmax(orc, am, y64[:M], absy[:M], f"lm head M={M}")
         say(f"  lm head M={M}: argmax {am.tolist()}, checked {n}/{M} rows")
+        # the seeded workload leaves row 0's top-2 gap above the bounds, so the
+        # oracle comparison (iv) binds on at least that row
+        assert n >= 1, f"lm head M={M}: no row with a top-2 gap above the bounds"
         # logits equal the dense product bit for bit
         ym = torch.empty((M, N), dtype=torch.float32, device="cuda")
         w4.w4a16_matmul(xd, dw.qw, dw.s, dw.b, ym)
         torch.cuda.synchronize()
         assert np.array_equal(host_f32(ym).view(np.uint32), y32.view(np.uint32))
+
+
+def test_lmhead_planted_maximum_and_ties_at_vocabulary_size(orc):
+    # the 262144 x 2560 head (the vocabulary-head schedule) with one planted
+    # maximum per activation row, each with an identical later copy: the copy
+    # ties bit for bit, and the lower index must win, wherever the two rows
+    # fall (same row group, next block, the far end of the vocabulary)
+    N, K = synthetic.LM_HEAD["N"], synthetic.LM_HEAD["K"]
+    w = synthetic.quantized_weights(N, K, seed=0, tag=(262144,), bias="exact")
+    x3 = synthetic.activations(3, K, seed=0, tag=(262144,))
+    xv = synthetic.bf16_values(x3)
+    star = [131071, 7, 200000]
+    dups = [N - 1, 8, 200000 + 37]
+    for m, (st, du) in enumerate(zip(star, dups)):
+        row = orc.pack_rows(np.where(xv[m] > 0, 15, 0).astype(np.uint8)[None, :])[0]
+        for n in (st, du):
+            w.qw[n] = row
+            w.scales[n] = w.scales[st]
+            w.biases[n] = w.biases[st]
+    say(f"lm head planted maxima {star} with later copies {dups}: oracle (all rows, M=3)")
+    y64, absy = oracle_qmm(orc, x3, w, workers=16)
+    for m in range(3):
+        best, gap = orc.argmax(y64[m])
+        assert best == star[m] and y64[m, dups[m]] == y64[m, star[m]], (m, best)
+        assert gap == 0.0                      # the copy ties exactly in the oracle too
+        rest = np.delete(y64[m], [star[m], dups[m]])
+        assert y64[m, star[m]] - rest.max() > 1e-3 * (absy[m, star[m]] + absy[m].max())
+    dw = DevWeights(w)
+    for M in synthetic.LM_HEAD["M"]:
+        say(f"  planted lm head M={M}")
+        am, logits = w4.lmhead_argmax(dev_bf16(x3[:M]), dw.qw, dw.s, dw.b, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        y = host_f32(logits)
+        for m in range(M):
+            assert int(am[m]) == star[m], (M, m, int(am[m]))
+            assert y[m, star[m]] == y[m, dups[m]]
+        check_f32(y, y64[:M], absy[:M], f"planted lm head M={M}")
 
 
 @pytest.mark.parametrize("N", [1, 100, 5000, 70000])
@@ -389,8 +443,9 @@ def routed_inputs(E, N, K, M, top_k, seed):
     return w, x, ids
 
 
-def run_id(dw_stack, x_bits, ids, N, f32=True, x_per_slot=False):
-    y = w4.matmul_id(dev_bf16(x_bits), dw_stack[0], dw_stack[1], dw_stack[2], dev_i32(ids), x_per_slot=x_per_slot,
+def run_id(dw_stack, x_bits, ids, N, f32=True):
+    """x_bits [M, K]: a token's slots share its row; [M, top_k, K]: one row per slot."""
+    y = w4.matmul_id(dev_bf16(x_bits), dw_stack[0], dw_stack[1], dw_stack[2], dev_i32(ids),
                      out_dtype=torch.float32 if f32 else torch.bfloat16)
     torch.cuda.synchronize()
     return host_f32(y) if f32 else host_bits(y)
@@ -454,9 +509,16 @@ def test_routed_variants(orc):
     say("routed: one input row per slot")
     xs = synthetic.activations(M * top_k, K, seed=10).reshape(M, top_k, K)
     y64s, abss = orc.qmm_id(xs, w.qw, w.scales, w.biases, ids, x_per_slot=True)
-    ys = run_id(stack, xs, ids, N, x_per_slot=True)
+    ys = run_id(stack, xs, ids, N)
     check_f32(ys, y64s, abss, "routed per-slot")
-    check_bf16(orc, run_id(stack, xs, ids, N, f32=False, x_per_slot=True), y64s, abss, K, "routed per-slot bf16")
+    check_bf16(orc, run_id(stack, xs, ids, N, f32=False), y64s, abss, K, "routed per-slot bf16")
+    say("routed: per-slot rows at a padded stride (K + 40) read the same values")
+    pad = torch.full((M, top_k, K + 40), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pad[:, :, :K] = dev_bf16(xs)
+    yp = torch.empty((M, top_k, N), dtype=torch.float32, device="cuda")
+    w4.w4a16_matmul_id(pad[:, :, :K], stack[0], stack[1], stack[2], dev_i32(ids), yp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(yp).view(np.uint32), ys.view(np.uint32))
     say("routed: out-of-range id fills its slot with NaN")
     bad = ids.copy()
     bad[1, 1] = E

@@ -33,10 +33,11 @@ MAX_N = 1 << 30         # W4A16_MAX_N
 MAX_K = 1 << 24         # W4A16_MAX_K
 
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN",
-          5: "ERR_WORKSPACE", 6: "ERR_HIP"}
+          5: "ERR_WORKSPACE", 6: "ERR_HIP", 7: "ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 1 << 20   # W4A16_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("w4a16_matmul", "w4a16_matmul_geglu", "w4a16_matmul_prefill", "w4a16_matmul_grouped", "w4a16_matmul_id", "w4a16_lmhead_argmax_workspace_bytes",
-           "w4a16_lmhead_argmax", "w4a16_dequant", "w4a16_gather_rows", "w4a16_pack", "w4a16_status_str",
+           "w4a16_lmhead_argmax", "w4a16_lmhead_argmax_noalloc", "w4a16_dequant", "w4a16_gather_rows", "w4a16_pack", "w4a16_status_str",
            "w4a16_abi_version", "w4a16_schedule_name")
 
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.w4a16_lmhead_argmax.restype = _int
         L.w4a16_lmhead_argmax.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _size, _int, _int,
                                           _int, _int, _vp]
+        L.w4a16_lmhead_argmax_noalloc.restype = _int
+        L.w4a16_lmhead_argmax_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _vp, _int, _int, _int, _int, _vp]
         L.w4a16_dequant.restype = _int
         L.w4a16_dequant.argtypes = [_vp, _vp, _vp, _vp, _int, _vp, _int, _int, _int, _vp]
         L.w4a16_gather_rows.restype = _int
@@ -304,6 +307,27 @@ def w4a16_lmhead_argmax(x, qw, scales, biases, logits, argmax, workspace, group:
     _check(lib().w4a16_lmhead_argmax(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(logits), code,
                                      _ptr(argmax), _ptr(workspace), workspace.numel(),
                                      M, N, K, group, _stream(stream)), "w4a16_lmhead_argmax")
+
+
+def w4a16_lmhead_argmax_noalloc(x, qw, scales, biases, logits, argmax, group: int = GROUP, stream=None,
+                                out_dtype=None) -> None:
+    """w4a16_lmhead_argmax with the library's built-in scratch instead of a
+    workspace: allocates nothing (calls overlapping on one GPU race)."""
+    M, K = _activations(x)
+    _dtype(qw, torch.int32, "qw")
+    N = qw.shape[0] if qw.dim() == 2 else -1
+    _weights(qw, scales, biases, N, K, group)
+    _dtype(argmax, torch.int32, "argmax")
+    _shape(argmax, (M,), "argmax")
+    if logits is not None:
+        code = _out_code(logits)
+        _shape(logits, (M, N), "logits")
+    else:
+        code = OUT_BF16 if out_dtype is None else out_dtype
+    _on_device(x, qw, scales, biases, logits, argmax)
+    _check(lib().w4a16_lmhead_argmax_noalloc(_ptr(x), _ptr(qw), _ptr(scales), _ptr(biases), _ptr(logits), code,
+                                             _ptr(argmax), M, N, K, group, _stream(stream)),
+           "w4a16_lmhead_argmax_noalloc")
 
 
 def _rows(rows, name="rows"):

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 #include "ops.hpp"
 #include "qmm_device.hpp"
@@ -260,6 +262,31 @@ w4a16_status_t lmhead_launch(const uint16_t* x, const uint32_t* qw, const uint16
   return launched(hipGetLastError());
 }
 
+// Scratch of w4a16_lmhead_argmax_noalloc: the per-block argmax keys, in a
+// file-scope device array (each GPU the library runs on holds its own copy
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// never the device memory: the device address is looked up once per device,
+// with that device current, and only that address is passed to kernels.
+static_assert(W4A16_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte lines");
+__device__ __align__(256) uint64_t scratch[W4A16_NOALLOC_SCRATCH_BYTES / sizeof(uint64_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t* g_scratch[kMaxDevices] = {};
+
+w4a16_status_t scratch_of_current_device(uint64_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W4A16_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W4A16_ERR_HIP;
+    g_scratch[dev] = static_cast<uint64_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return W4A16_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -297,6 +324,7 @@ const char* w4a16_status_str(w4a16_status_t s) {
     case W4A16_ERR_ALIGN: return "pointer misaligned";
     case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
     case W4A16_ERR_HIP: return "HIP runtime rejected the launch";
+    case W4A16_ERR_SCRATCH: return "problem needs more than the library's built-in scratch (W4A16_NOALLOC_SCRATCH_BYTES)";
     case W4A16_STATUS_MAX_ENUM: break;
   }
   return "unknown status";
@@ -435,6 +463,19 @@ w4a16_status_t w4a16_lmhead_argmax(const uint16_t* x, const uint32_t* qw, const 
   if (!aligned(workspace, 8)) return W4A16_ERR_ALIGN;
   return lmhead_launch(x, qw, scales, biases, logits, out_dtype, argmax, reinterpret_cast<uint64_t*>(workspace), M,
                        N, K, group, (hipStream_t)stream);
+}
+
+w4a16_status_t w4a16_lmhead_argmax_noalloc(const uint16_t* x, const uint32_t* qw, const uint16_t* scales,
+                                           const uint16_t* biases, void* logits, int out_dtype, int32_t* argmax,
+                                           int M, int N, int K, int group, void* stream) {
+  w4a16_status_t st = check_lmhead(x, qw, scales, biases, logits, out_dtype, argmax, M, N, K, group);
+  if (st != W4A16_OK || M == 0 || N == 0) return st;
+  if (w4a16_lmhead_argmax_workspace_bytes(M, N, K, group) > W4A16_NOALLOC_SCRATCH_BYTES) return W4A16_ERR_SCRATCH;
+  uint64_t* partial = nullptr;
+  st = scratch_of_current_device(&partial);
+  if (st != W4A16_OK) return st;
+  return lmhead_launch(x, qw, scales, biases, logits, out_dtype, argmax, partial, M, N, K, group,
+                       (hipStream_t)stream);
 }
 
 w4a16_status_t w4a16_dequant(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, const int32_t* rows,

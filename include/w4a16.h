@@ -69,6 +69,7 @@ extern "C" {
 #define W4A16_MAX_GROUP 8
 #define W4A16_MAX_N (1 << 30)
 #define W4A16_MAX_K (1 << 24)
+#define W4A16_NOALLOC_SCRATCH_BYTES (1 << 20)
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
@@ -81,6 +82,8 @@ typedef enum w4a16_status {
     W4A16_ERR_ALIGN = 4,       /* a pointer violates the alignment above */
     W4A16_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     W4A16_ERR_HIP = 6,         /* the HIP runtime rejected a launch */
+    W4A16_ERR_SCRATCH = 7,     /* a no-allocation entry point's problem needs more than
+                                  W4A16_NOALLOC_SCRATCH_BYTES of built-in scratch */
     W4A16_STATUS_MAX_ENUM = 0x7FFFFFFF  /* not a status: gives the type the range of a 32-bit
                                            int, so any value a caller passes back to
                                            w4a16_status_str is a valid value of it */
@@ -212,6 +215,28 @@ w4a16_status_t w4a16_lmhead_argmax(const uint16_t *x, const uint32_t *qw, const 
                                    const uint16_t *biases, void *logits, int out_dtype,
                                    int32_t *argmax, void *workspace, size_t workspace_bytes,
                                    int M, int N, int K, int group, void *stream);
+
+/*
+ * w4a16_lmhead_argmax without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * w4a16_lmhead_argmax; the per-block argmax keys go to a scratch array built
+ * into the library (W4A16_NOALLOC_SCRATCH_BYTES on each GPU, held until the
+ * process ends; its device address is looked up on the first call on each
+ * device).  Nothing is allocated.  A problem whose workspace
+ * (w4a16_lmhead_argmax_workspace_bytes) exceeds the scratch returns
+ * W4A16_ERR_SCRATCH before anything is enqueued (1 MiB covers a 262144-row
+ * vocabulary at every M).  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap in time on one GPU (concurrent streams, or host threads
+ * enqueueing onto different streams) race and must be serialized by the
+ * caller; calls in order on one stream are safe.  Nothing carries over from
+ * one call to the next (every key the finalize reads is written by the same
+ * call), so the scratch needs no clearing.
+ */
+w4a16_status_t w4a16_lmhead_argmax_noalloc(const uint16_t *x, const uint32_t *qw, const uint16_t *scales,
+                                           const uint16_t *biases, void *logits, int out_dtype,
+                                           int32_t *argmax, int M, int N, int K, int group,
+                                           void *stream);
 
 /*
  * Dequantized weights out[r][k] = fma(s, q, b) in fp32 for rows[r] (rows ==

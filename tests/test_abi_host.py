@@ -15,7 +15,7 @@ import decode_w4a16_affine_amd as w4
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = range(7)
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, ESCRATCH = range(8)
 A16 = 0x10000          # 16-byte aligned fake address
 A4 = 0x20004           # 4-byte aligned only
 
@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(L):
 def test_abi_version_and_status_strings(L):
     assert w4.w4a16_abi_version() == 2
     seen = set()
-    for s in range(7):
+    for s in range(8):
         txt = w4.w4a16_status_str(s)
         assert txt and txt not in seen
         seen.add(txt)
@@ -215,6 +215,31 @@ def test_lmhead_workspace_rules(L):
     assert lm(am=A16 + 2) == EALIGN
     assert lm(logits=A16 + 2, out=1) == EALIGN
     assert lm(group=256) == EUNSUP
+
+
+def test_lmhead_noalloc_validation(L):
+    # the same checks as the workspace entry point, and a size limit instead of
+    # the workspace: problems needing more keys than the built-in scratch are
+    # refused before anything touches HIP
+    def na(x=A16, qw=A16, am=A16, logits=None, M=1, N=1000, K=512, group=64, out=0):
+        return L.w4a16_lmhead_argmax_noalloc(x, qw, A16, A16, logits, out, am, M, N, K, group, None)
+
+    assert na(group=32) == EUNSUP
+    assert na(M=9) == EUNSUP
+    assert na(N=2 ** 31 - 1) == ESHAPE
+    assert na(K=100) == ESHAPE
+    assert na(x=None) == ENULL
+    assert na(am=None) == ENULL
+    assert na(qw=A4) == EALIGN
+    assert na(am=A16 + 2) == EALIGN
+    assert na(logits=A16 + 2, out=1) == EALIGN
+    assert na(x=None, M=0) == OK
+    big = w4.MAX_N
+    assert L.w4a16_lmhead_argmax_workspace_bytes(8, big, 64, 64) > w4.NOALLOC_SCRATCH_BYTES
+    assert na(M=8, N=big, K=64) == ESCRATCH
+    # the 262144-row vocabulary fits the scratch at every M
+    for M in range(1, 9):
+        assert 0 < L.w4a16_lmhead_argmax_workspace_bytes(M, 262144, 2560, 64) <= w4.NOALLOC_SCRATCH_BYTES, M
 
 
 def test_dequant_gather_and_pack_reject_bad_arguments(L):

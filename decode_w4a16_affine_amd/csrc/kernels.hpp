@@ -306,7 +306,9 @@ __device__ __forceinline__ void routed_pass(const int* list, const uint16_t* x, 
     yoff[i] = (size_t)sl * src.N;
   }
   float acc[R][C];
-  block_rows<C, R, CPL, KSPLIT, PRE, DEPTH, 1, G>(acc, xr, src, block_row0, xs, red);
+  // default cache policy: an expert serving more than two tokens is streamed
+  // once per two-row pass (nontemporal loads measured no faster here)
+  block_rows<C, R, CPL, KSPLIT, PRE, DEPTH, 1, G, kPadDefault<C, KSPLIT>, false>(acc, xr, src, block_row0, xs, red);
   store_to<C, R, KSPLIT>(acc, RM::first_row(block_row0), src.N, y, yoff, out_f32);
 }
 

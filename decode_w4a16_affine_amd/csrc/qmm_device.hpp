@@ -226,15 +226,26 @@ struct WaveRows {
 // conflict cycles per LDS instruction in the K-split kernels).  With CS + 2,
 // lane (c, q) lands on bank slot 4q + c (mod 16), all distinct; reads (16
 // consecutive chunks of one piece) stay conflict-free.  PAD selects the
-// padded stride; the kernels pad for M <= 2 (kPadDefault), where it measured
-// 1-4% faster (M = 1 step, gate+up, o, M = 2 step); for M >= 3 the larger tile
-// cost a block per CU in some schedules (gate+up at M = 5 10% slower) and the
-// M = 3 and 5 steps 2% slower.  The LM head never pads (same-box A/B: M = 1
-// unchanged, M = 3 113 -> 109.5 us unpadded).
+// padded stride; the kernels pad for M <= 2 and for every K-split schedule
+// (kPadDefault): unsplit rows at M >= 3 lost a block per CU to the larger
+// tile (gate+up at M = 5 10% slower), while the K-split blocks keep their
+// occupancy and gain (same-box A/B, us: o at M = 5 6.83 -> 6.25, q/k/v 7.28 ->
+// 6.88, down 16.1 -> 15.6; M = 3 o 5.00 -> 4.81).  The LM head never pads
+// (same-box A/B: M = 1 unchanged, M = 3 113 -> 109.5 us unpadded).
 template <int CS, bool PAD>
 constexpr int kPieceStride = PAD ? CS + 2 : CS;
-template <int M>
-constexpr bool kPadDefault = M <= 2;
+template <int M, int KSPLIT = 1>
+constexpr bool kPadDefault = M <= 2 || KSPLIT > 1;
+
+// Cache policy of the weight loads.  Each weight is read once per call, and
+// loads marked nontemporal measured faster for the long streams (same-box A/B,
+// us: square 16384^2 M = 1 31.3 -> 29.6, LM-head product 65.9 -> 63.2,
+// gate+up 8.31 -> 7.99, down 6.04 -> 5.91; a plain 1 GiB read 6.5 -> 7.2
+// TB/s) but slower for the short K-split-5 matrices (q/k/v/o +3-5%) and the
+// same for the routed product; scales and biases marked so were slower
+// everywhere.  Buffer-load cache-policy operand: bit 1 = nt.
+template <int KSPLIT>
+constexpr bool kNtDefault = KSPLIT != 5;
 
 // Activations of one K-tile as fp32 in LDS.  Layout (float4 units):
 // xs[(m * 8 + piece) * PS + c] holds k = k0 + 32c + 4 piece .. +3 (PS: the
@@ -263,7 +274,7 @@ __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, f
 // skipped.  The staging and chunk body are those of x_stage_tile and
 // consume_slot written out in place (through the helpers the compiler
 // allocated 44-71% more registers for the K-split kernels).
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS, int G, bool PAD>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, bool FULL, int RS, int G, bool PAD, bool NTLOAD>
 __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w, int k0,
                                           int klen, float4* xs) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -305,7 +316,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
       const bool ok = FULL || L + j * LPR < cseg;
       const uint32_t oq = ok ? qb[r] + (uint32_t)(j * LPR * 16) : kOffNone;
       const uint32_t og = ok ? gb[r] + (uint32_t)(j * LPR / kChunksPerGroup<G>) * 2u : kOffNone;
-      tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, 0));
+      tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, NTLOAD ? 2 : 0));
       tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
       tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
     }
@@ -368,7 +379,7 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 template <int M, int CPL, int KSPLIT>
 constexpr bool kRolled = KSPLIT == 1 && 2 * M * 8 * CPL * kRowLanes * 16 <= 32768;
 // float4 of LDS a block needs for its activation tiles
-template <int M, int CPL, int KSPLIT, bool PAD = kPadDefault<M>>
+template <int M, int CPL, int KSPLIT, bool PAD = kPadDefault<M, KSPLIT>>
 constexpr int kXsF4 = M * 8 * kPieceStride<CPL * kRowLanes * KSPLIT, PAD> * (kRolled<M, CPL, KSPLIT> ? 2 : 1);
 
 // The first `ntiles` (>= 2) full K-tiles of the rows, without a K-split, as one
@@ -382,7 +393,7 @@ constexpr int kXsF4 = M * 8 * kPieceStride<CPL * kRowLanes * KSPLIT, PAD> * (kRo
 // vmcnt waits stay chunk-exact.  Every lane consumes the same chunks in the same
 // order with the same body as tile_pass: the sums are bitwise those of the
 // tile-by-tile walk.  xs must hold 2 * M * 8 * CPL * 16 float4.
-template <int M, int R, int CPL, int PRE, int DEPTH, int G, bool PAD>
+template <int M, int R, int CPL, int PRE, int DEPTH, int G, bool PAD, bool NTLOAD>
 __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w,
                                              int ntiles, float4* xs) {
   constexpr int LPR = kRowLanes;
@@ -424,7 +435,7 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
       const uint32_t step = (uint32_t)((next ? CS : 0) + j * LPR);
       const uint32_t oq = live ? qb[r] + step * 16u : kOffNone;
       const uint32_t og = live ? gb[r] + step / kChunksPerGroup<G> * 2u : kOffNone;
-      tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, 0));
+      tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, NTLOAD ? 2 : 0));
       tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
       tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
     }
@@ -480,7 +491,8 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 // KSPLIT == S > 1: the S waves of a row set share its rows; on return every
 //              lane of those waves holds the sums (combined in wave order).
 // xs must hold kXsF4<M, CPL, KSPLIT, PAD> float4.  Call with all threads (barriers).
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS = 1, int G = 64, bool PAD = kPadDefault<M>>
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS = 1, int G = 64,
+          bool PAD = kPadDefault<M, KSPLIT>, bool NTLOAD = kNtDefault<KSPLIT>>
 __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& xr, const RowSrc& src,
                                            int block_row0, float4* xs, float* red) {
   constexpr int LPR = kRowLanes * KSPLIT;
@@ -513,16 +525,16 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
   if constexpr (kRolled<M, CPL, KSPLIT>) {
     const int nfull = K / KTILE;
     if (nfull >= 2) {
-      rolled_tiles<M, R, CPL, PRE, DEPTH, G, PAD>(acc, xr, w, nfull, xs);
+      rolled_tiles<M, R, CPL, PRE, DEPTH, G, PAD, NTLOAD>(acc, xr, w, nfull, xs);
       kr = nfull * KTILE;
     }
   }
   for (int k0 = kr; k0 < K; k0 += KTILE) {
     const int klen = min(KTILE, K - k0);
     if (klen == KTILE)
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true, RS, G, PAD>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, true, RS, G, PAD, NTLOAD>(acc, xr, w, k0, klen, xs);
     else
-      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false, RS, G, PAD>(acc, xr, w, k0, klen, xs);
+      tile_pass<M, R, CPL, KSPLIT, PRE, DEPTH, false, RS, G, PAD, NTLOAD>(acc, xr, w, k0, klen, xs);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)

@@ -7,11 +7,16 @@ HBM bytes with the factor that a device-to-device copy of known size reads on
 the same counter (the benchmark's ``--calibrate-copy`` phase runs one).
 
     python -m decode_w4a16_affine_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
+    python -m decode_w4a16_affine_amd.profiling trace  <kernel_trace.csv> <out.md> "<command>" [kernel]
     python -m decode_w4a16_affine_amd.profiling traffic <fetch.csv> <write.csv> <out.json> "<fetch cmd>" "<write cmd>"
+    python -m decode_w4a16_affine_amd.profiling traffic-md <traffic.json> <out.md>
     python -m decode_w4a16_affine_amd.profiling sq <counter_collection.csv>[,<more.csv>] <out.md> "<command>"
     python -m decode_w4a16_affine_amd.profiling prefill-workload [M]
+    python -m decode_w4a16_affine_amd.profiling configs-workload
 
-``prefill-workload`` runs the prefill products of the decode stack's gate+up
+``configs-workload`` runs every configuration's decode kernels a few times on
+cold weights, then the calibration copy (the program for the counter passes of
+the configuration kernels).  ``prefill-workload`` runs the prefill products of the decode stack's gate+up
 and down shapes at M rows (default 4096; four eager calls each, seeded
 synthetic inputs): the program to run under ``rocprofv3 --pmc`` for the
 matrix-core kernels.
@@ -33,7 +38,7 @@ KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in
 PROBE_LIB = os.path.join(HERE, "libw4a16_probe.so")
 
 
-def stream_read(torch, src, sink, blocks: int = 0, stream=None) -> None:
+def stream_read(torch, src, sink, blocks: int = 0, nontemporal: bool = True, stream=None) -> None:
     """One launch of the 128-bit streaming-read kernel (include/w4a16_probe.h) over
     the bytes of the contiguous device tensor `src`; `sink` a 4-byte device tensor."""
     import ctypes
@@ -47,13 +52,13 @@ def stream_read(torch, src, sink, blocks: int = 0, stream=None) -> None:
         _probe = ctypes.CDLL(PROBE_LIB)
         _probe.w4a16_probe_stream_read.restype = ctypes.c_int
         _probe.w4a16_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                                   ctypes.c_void_p]
+                                                   ctypes.c_int, ctypes.c_void_p]
     if not (src.is_cuda and src.is_contiguous() and sink.is_cuda):
         raise ValueError("stream_read takes contiguous device tensors")
     nbytes = src.numel() * src.element_size()
     st = (stream or torch.cuda.current_stream()).cuda_stream
     rc = _probe.w4a16_probe_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
-                                        blocks, ctypes.c_void_p(st))
+                                        blocks, int(bool(nontemporal)), ctypes.c_void_p(st))
     if rc != 0:
         raise RuntimeError(f"w4a16_probe_stream_read failed: hipError {rc}")
 COPY_BYTES = 256 << 20
@@ -74,6 +79,27 @@ def short_name(name: str) -> str:
     return m.group(1) if m else name.split("(")[0][:80]
 
 
+def _ours(name: str) -> bool:
+    """A kernel of this library (not a runtime copy or a torch kernel)."""
+    return short_name(name) != name.split("(")[0][:80] or "qmm_" in name
+
+
+def traffic_markdown(record_json: str, out_md: str) -> None:
+    """The traffic record as a table: HBM bytes per launch by kernel and grid."""
+    rec = json.load(open(record_json))
+    lines = ["# HBM traffic per launch (rocprofv3 counters)", "",
+             f"FETCH_SIZE: `{rec['fetch_command']}`", "", f"WRITE_SIZE: `{rec['write_command']}`", "",
+             f"Counter bytes are scaled by the reading of a {rec['copy_bytes'] >> 20} MiB device copy in the same run: "
+             f"fetch x{rec['fetch_factor']}, write x{rec['write_factor']}.  Kernel sources: sha256 "
+             f"{rec['source_sha256'][:16]}.", "",
+             "| kernel | grid (work-items) | fetched bytes | written bytes | HBM bytes |", "|---|---|---|---|---|"]
+    for k, d in rec["kernels"].items():
+        for g, v in d.items():
+            lines.append(f"| `{k}` | {g} | {v['fetch_bytes']:,} | {v['write_bytes']:,} | {v['hbm_bytes']:,} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
@@ -83,6 +109,58 @@ def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f}% |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
+
+
+def summarize_trace(trace_csv: str, out_md: str, command: str, focus: str = "") -> dict:
+    """Per-kernel distribution of the dispatch durations in a rocprofv3 kernel
+    trace, and for each kernel the launch period of back-to-back dispatches
+    of that kernel (start to next start when no other kernel ran between: the
+    duration plus the gap a graph leaves before the next launch, which is what
+    events around a graph of consecutive launches measure)."""
+    import numpy as np
+
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("Name") or ""
+            st = int(r.get("Start_Timestamp") or r.get("Begin_Ns") or 0)
+            en = int(r.get("End_Timestamp") or r.get("End_Ns") or 0)
+            rows.append((st, en, short_name(name)))
+    rows.sort()
+    dur, period = {}, {}
+    for i, (st, en, k) in enumerate(rows):
+        dur.setdefault(k, []).append((en - st) / 1e3)
+        if i + 1 < len(rows) and rows[i + 1][2] == k:
+            period.setdefault(k, []).append((rows[i + 1][0] - st) / 1e3)
+    total = sum(sum(v) for v in dur.values()) or 1.0
+    order = sorted(dur, key=lambda k: -sum(dur[k]))
+    lines = ["# rocprofv3 kernel trace: dispatch durations", "", f"Command: `{command}`", "",
+             "Durations are end minus start of each dispatch (us).  The launch period is start to next start",
+             "over pairs of consecutive dispatches of the same kernel (graph replays of one projection's",
+             "launches), i.e. the duration plus the gap before the next launch.", "",
+             "| kernel | calls | mean | p10 | median | p90 | share | back-to-back pairs | median launch period |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    summary = {}
+    for k in order:
+        d = np.array(dur[k])
+        pr = np.array(period.get(k, []))
+        q = np.percentile(d, [10, 50, 90])
+        summary[k] = dict(calls=int(d.size), mean_us=float(d.mean()), p10_us=float(q[0]), median_us=float(q[1]),
+                          p90_us=float(q[2]), pairs=int(pr.size),
+                          period_median_us=float(np.median(pr)) if pr.size else None)
+        per = f"{np.median(pr):.3f}" if pr.size else "-"
+        lines.append(f"| `{k}` | {d.size} | {d.mean():.3f} | {q[0]:.3f} | {q[1]:.3f} | {q[2]:.3f} | "
+                     f"{100 * d.sum() / total:.2f}% | {pr.size} | {per} |")
+        if len(lines) > 60:
+            break
+    if focus:
+        for k, v in summary.items():
+            if k == focus:
+                lines += ["", f"Focus `{k}`: mean {v['mean_us']:.3f} us, median {v['median_us']:.3f} us, "
+                              f"median launch period {v['period_median_us']} us over {v['pairs']} pairs."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return summary
 
 
 def _per_dispatch(path: str, counter: str):
@@ -110,7 +188,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_json: str, fetch_cmd: 
     for rows, key, fac in ((fr, "fetch_bytes", ff), (wr, "write_bytes", wf)):
         groups = {}
         for n, g, v in rows:
-            if "qmm_" not in n:
+            if not _ours(n):
                 continue
             groups.setdefault((short_name(n), g), []).append(v * fac)
         for (k, g), vals in groups.items():
@@ -183,6 +261,102 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+def configs_workload(calls: int = 3) -> None:
+    """The configurations' kernels, a few eager calls each on rotated weight
+    copies (cold weights), then a 256 MiB device copy (the counters' byte
+    calibration): the program to run under ``rocprofv3 --pmc``.  Covers the
+    decode projections at M = 1, 2, 3, 5, the tied LM head (argmax) at M = 1
+    and 3, the square matrix at M = 1, 4, 8, the routed stack at M = 1 and 8,
+    GeGLU on the gate+up matrix at M = 1 and 5 and the row gather."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    import numpy as np
+    import torch
+
+    import decode_w4a16_affine_amd as w4
+    import synthetic
+
+    def dev(w, copies, shape=None):
+        qw0 = torch.from_numpy(w.qw.view(np.int32)).cuda()
+        s0 = torch.from_numpy(w.scales.view(np.int16)).view(torch.bfloat16).cuda()
+        b0 = torch.from_numpy(w.biases.view(np.int16)).view(torch.bfloat16).cuda()
+        if shape is not None:
+            qw0, s0, b0 = qw0.view(shape[0]), s0.view(shape[1]), b0.view(shape[1])
+        out = []
+        for c in range(copies):
+            key = int(np.array([(0x9E3779B9 * c) & 0xFFFFFFFF], dtype=np.uint32).view(np.int32)[0])
+            out.append((qw0 ^ key, s0.clone(), b0.clone()))
+        return out
+
+    def xs(M, K, tag):
+        return torch.from_numpy(synthetic.activations(M, K, seed=0, tag=tag).view(np.int16)).view(torch.bfloat16).cuda()
+
+    for name in synthetic.LAYER_ORDER:
+        N, K = synthetic.PROJECTIONS[name]
+        mats = dev(synthetic.quantized_weights(N, K, seed=0, tag=(N, 21)), 24)
+        for M in (1, 2, 3, 5):
+            x = xs(M, K, (N, 21))
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            for i in range(calls * 8):
+                q, sc, bi = mats[i % len(mats)]
+                w4.w4a16_matmul(x, q, sc, bi, y)
+        torch.cuda.synchronize()
+        print(f"{name}: done", flush=True)
+        del mats
+    t = synthetic.LM_HEAD
+    N, K = t["N"], t["K"]
+    mats = dev(synthetic.quantized_weights(N, K, seed=0, tag=(N,), bias="exact"), 3)
+    for M in t["M"]:
+        x = xs(M, K, (N,))
+        for i in range(calls):
+            q, sc, bi = mats[i % 3]
+            w4.lmhead_argmax(x, q, sc, bi)
+        rows = torch.arange(0, N, N // 4096, dtype=torch.int32, device="cuda")
+        w4.gather_rows(q, sc, bi, rows)
+    torch.cuda.synchronize()
+    print("lm head: done", flush=True)
+    del mats
+    t = synthetic.SQUARE
+    mats = dev(synthetic.quantized_weights(t["N"], t["K"], seed=0, tag=(t["N"],)), 4)
+    for M in t["M"]:
+        x = xs(M, t["K"], (t["N"],))
+        for i in range(calls):
+            q, sc, bi = mats[i % 4]
+            w4.matmul(x, q, sc, bi)
+    torch.cuda.synchronize()
+    print("square: done", flush=True)
+    del mats
+    t = synthetic.MOE
+    E, N, K, top_k = t["E"], t["N"], t["K"], t["top_k"]
+    mats = dev(synthetic.quantized_weights(E * N, K, seed=0, tag=(E,)), 3, shape=((E, N, K // 8), (E, N, K // 64)))
+    for M in t["M"]:
+        ids = torch.from_numpy(synthetic.expert_ids(M, top_k, E, seed=0)).cuda()
+        x = xs(M, K, (E,))
+        for i in range(calls):
+            q, sc, bi = mats[i % 3]
+            w4.matmul_id(x, q, sc, bi, ids)
+    torch.cuda.synchronize()
+    print("routed: done", flush=True)
+    del mats
+    N, K = synthetic.PROJECTIONS["gate_up"]
+    mats = dev(synthetic.quantized_weights(N, K, seed=0, tag=(N, 11)), 12)
+    for M in (1, 5):
+        x = xs(M, K, (N, 11))
+        h = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
+        for i in range(calls * 4):
+            q, sc, bi = mats[i % len(mats)]
+            w4.w4a16_matmul_geglu(x, q, sc, bi, h)
+    torch.cuda.synchronize()
+    print("geglu: done", flush=True)
+    del mats
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("calibration copy: done", flush=True)
+
+
 def prefill_workload(M: int = 4096) -> None:
     """Four eager prefill calls on each of the gate+up and down shapes at M rows."""
     sys.path.insert(0, os.path.dirname(HERE))
@@ -207,14 +381,20 @@ def prefill_workload(M: int = 4096) -> None:
 
 
 if __name__ == "__main__":
-    if len(sys.argv) >= 2 and sys.argv[1] == "prefill-workload":
+    if len(sys.argv) >= 2 and sys.argv[1] == "configs-workload":
+        configs_workload()
+    elif len(sys.argv) >= 2 and sys.argv[1] == "prefill-workload":
         prefill_workload(int(sys.argv[2]) if len(sys.argv) >= 3 else 4096)
     elif len(sys.argv) >= 2 and sys.argv[1] == "stats":
         summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif len(sys.argv) >= 2 and sys.argv[1] == "trace":
+        summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5] if len(sys.argv) >= 6 else "")
     elif len(sys.argv) >= 2 and sys.argv[1] == "sq":
         summarize_sq(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 2 and sys.argv[1] == "traffic":
         print(json.dumps(summarize_traffic(*sys.argv[2:7]), indent=1))
+    elif len(sys.argv) >= 2 and sys.argv[1] == "traffic-md":
+        traffic_markdown(sys.argv[2], sys.argv[3])
     else:
         print(__doc__)
         sys.exit(2)

@@ -18,16 +18,19 @@ extern "C" {
 
 /*
  * Reads `bytes` bytes at `src` (device memory, 16-byte aligned, bytes a
- * multiple of 16) once with 16-byte loads: each thread keeps four loads in
- * flight, consecutive lanes read consecutive 16-byte pieces.  The loaded
- * words are folded into one value per thread, which is stored to sink[0]
- * only if it equals a constant no input of this benchmark produces (the
- * store keeps the loads alive and never happens in practice).
- * blocks: workgroups of 256 threads (0 = 16 per compute unit of device 0).
+ * multiple of 16) once with 16-byte loads: a grid-stride loop in which each
+ * thread keeps two loads in flight and consecutive lanes read consecutive
+ * 16-byte pieces; nontemporal != 0 marks the loads nontemporal (streamed data
+ * that should not displace cached lines).  The loaded words are folded into
+ * one value per thread, which is stored to sink[0] only if it equals a
+ * constant no input of this benchmark produces (the store keeps the loads
+ * alive and never happens in practice).
+ * blocks: workgroups of 256 threads (0 = 3 per compute unit of device 0).
  * Returns 0, or a nonzero hipError_t value if the arguments are invalid
  * (NULL, misaligned, bytes not a multiple of 16) or the launch failed.
  */
-int w4a16_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks, void *stream);
+int w4a16_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks, int nontemporal,
+                            void *stream);
 
 #ifdef __cplusplus
 }

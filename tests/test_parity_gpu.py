@@ -698,6 +698,44 @@ def test_prefill_zero_weight_rows_exact(orc, M, N, K):
     check_f32(y32[:, rows], y64, absy, "prefill zero rows")
 
 
+@pytest.mark.parametrize("M,N,K", [(20, 64, 2560), (256, 4096, 2560), (1024, 4096, 1280)])
+def test_prefill_cancelling_rows_within_the_documented_bounds(orc, M, N, K):
+    # rows whose every code is 15 with b = -15 s (s a power of two, so b is
+    # exact in bf16) dequantize to w = 0 exactly: the oracle gives 0 with a
+    # bound of 0.  The per-wave form (M = 20) splits each w into bf16 parts and
+    # returns exactly 0.  The LDS-tiled forms (64 and 256 tiles) use the
+    # rearranged sums s * sum(x (q - 8)) + (b + 8 s) * sum(x), whose rounding is
+    # bounded on sum |s x (q - 8)| + |(b + 8 s) x| instead (the documented
+    # bound of w4a16_matmul_prefill): their residue must stay within 1e-3 of
+    # that sum.  The other rows keep the usual bound.
+    w = synthetic.quantized_weights(N, K, seed=N + 9, bias="exact")
+    cancel = np.arange(1, N, 5)
+    w.qw[cancel] = 0xFFFFFFFF
+    s_pow2 = synthetic.bf16_bits(np.float32(2.0 ** 10))
+    b_neg = synthetic.bf16_bits(np.float32(-15.0 * 2.0 ** 10))
+    w.scales[cancel] = s_pow2
+    w.biases[cancel] = b_neg
+    x = synthetic.activations(M, K, seed=M + 9)
+    tiled = M >= 32
+    say(f"prefill cancelling rows M={M} N={N} K={K} ({'tiled' if tiled else 'per-wave'} form)")
+    y32 = run_prefill(DevWeights(w), x, N, f32=True)
+    y64, absy = oracle_qmm(orc, x, w, rows=cancel.astype(np.int32))
+    assert np.all(y64 == 0) and np.all(absy == 0)
+    got = y32[:, cancel].astype(np.float64)
+    assert np.all(np.isfinite(got))
+    if not tiled:
+        assert np.all(got == 0), int(np.count_nonzero(got))
+    else:
+        # sum_k |s x (q - 8)| + |(b + 8 s) x| with q = 15, s = 2^10, b + 8 s = -7 * 2^10
+        xs = np.abs(synthetic.bf16_values(x).astype(np.float64)).sum(axis=1)
+        weak = (2.0 ** 10 * 7 + 7 * 2.0 ** 10) * xs
+        assert np.all(np.abs(got) <= 1e-3 * weak[:, None]), float(np.max(np.abs(got) / weak[:, None]))
+        say(f"  largest residue / weak bound sum: {float(np.max(np.abs(got) / weak[:, None])):.2e}")
+    others = np.setdiff1d(np.arange(0, N, max(1, N // 150)), cancel).astype(np.int32)
+    y64o, abso = oracle_qmm(orc, x, w, rows=others)
+    check_f32(y32[:, others], y64o, abso, "prefill cancelling, other rows")
+
+
 @pytest.mark.parametrize("M,N,K", [(13, 2560, 10240), (16, 20480, 2560), (9, 5000, 640)])
 def test_prefill_small_M_is_the_decode_path(orc, M, N, K):
     # up to 16 rows the prefill entry runs the decode kernels on chunks of at

@@ -66,7 +66,7 @@ struct PrefillStep {
 // KW = 4: the four waves own the same output tile and take every fourth K
 // step, and their partial sums are added in wave order through LDS (for
 // problems too small to fill the GPU otherwise).  Each wave keeps the loads of
-// its next K step in flight while it computes the current one.
+// its next two K steps in flight while it computes the current one.
 template <int TM, int TN, int KW, int G>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
@@ -118,29 +118,57 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
 #pragma unroll
     for (int u = 0; u < TN; ++u) acc[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  PrefillStep<TM, TN> cur, nxt;
-  load(wk, cur);
-  for (int st = wk; st < steps; st += KW) {
-    load(st + KW, nxt);
+  // A ring of PD steps of operands, PD - 1 steps of loads in flight, named at
+  // compile time (the loop is unrolled by PD), so nothing is copied at the back
+  // edge: a carried operand set that was copied from the freshly loaded one
+  // made the compiler wait for all loads at the end of every step
+  // (vmcnt(0), 0.4 loads outstanding on average).  Same-box A/B against that
+  // loop (us, per-wave form): down 2560 <- 10240 M = 32 / 64 / 128 / 256 81.9 /
+  // 99.6 / 98.8 / 179 -> 80.3 / 95.7 / 93.8 / 177, gate+up M = 24 48.5 -> 45.7;
+  // four or six steps in flight were no faster.  The plain or fast
+  // dequantization is chosen per wave (both give the same bits).
+  constexpr int PD = 3;
+  PrefillStep<TM, TN> buf[PD];
+#pragma unroll
+  for (int i = 0; i < PD - 1; ++i) load(wk + i * KW, buf[i]);
+  auto compute = [&](const PrefillStep<TM, TN>& c) {
+    float sv[TN], bv[TN];
+    bool plain = false;
 #pragma unroll
     for (int u = 0; u < TN; ++u) {
-      const float sv = bf16_lo(cur.s[u]);
-      const float bv = bf16_lo(cur.b[u]);
+      sv[u] = bf16_lo(c.s[u]);
+      bv[u] = bf16_lo(c.b[u]);
+      plain |= needs_plain(sv[u]);
+    }
+    const bool any_plain = __any(plain);
+#pragma unroll
+    for (int u = 0; u < TN; ++u) {
       float d[8];
-      if (needs_plain(sv))
-        dequant8_plain(cur.w[u], sv, bv, d);
+      if (any_plain)
+        dequant8_plain(c.w[u], sv[u], bv[u], d);
       else
-        dequant8_fast(cur.w[u], sv * 0x1p24f, sv * 0x1p20f, bv, d);
+        dequant8_fast(c.w[u], sv[u] * 0x1p24f, sv[u] * 0x1p20f, bv[u], d);
       bf16x8_t hi, lo;
       split_bf16(d, hi, lo);
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[t], hi, acc[t][u], 0, 0, 0);
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[t], lo, acc[t][u], 0, 0, 0);
+        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.a[t], hi, acc[t][u], 0, 0, 0);
+        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.a[t], lo, acc[t][u], 0, 0, 0);
       }
     }
-    cur = nxt;
+  };
+  int st = wk;
+  for (; st + (PD - 1) * KW < steps; st += PD * KW) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      load(st + (j + PD - 1) * KW, buf[(j + PD - 1) % PD]);
+      compute(buf[j]);
+    }
   }
+  // the last steps (fewer than PD): their loads are already in flight
+#pragma unroll
+  for (int j = 0; j < PD - 1; ++j)
+    if (st + j * KW < steps) compute(buf[j]);
 
   if (KW > 1) {
     // waves 1..KW-1 hand their partial sums to wave 0, which adds them in order

@@ -84,16 +84,17 @@ struct Sched<M, 5, CLS> {
 
 // The routed product streams one expert's rows per distinct expert in the ids,
 // so without a K-split its grid holds many experts' rows: two rows per lane
-// (measured on 64 experts of 6144 x 2048 with top-8 routing: M = 8 90.5 ->
-// 74.5 us, M = 1 13.2 -> 12.8 us).  Passes of at most two activation rows
-// (most experts serve one or two tokens; four-row passes cost occupancy).
+// for passes of two activation rows (measured on 64 experts of 6144 x 2048
+// with top-8 routing: M = 8 90.5 -> 74.5 us), one for single-token launches
+// (same-box A/B, M = 1: 14.37 -> 13.49 us).  Passes of at most two activation rows (most
+// experts serve one or two tokens; four-row passes cost occupancy).
 template <int MB, int KSPLIT, int CLS>
 struct RoutedSched : Sched<MB, KSPLIT, CLS> {
   static constexpr int RS = 1;
 };
 template <int MB, int CLS>
 struct RoutedSched<MB, 1, CLS> {
-  static constexpr int R = 2;
+  static constexpr int R = MB == 1 ? 1 : 2;
   static constexpr int CPL = Sched<MB, 1, CLS | 4>::CPL;
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 2;

@@ -36,11 +36,10 @@ inline int ksplit_for(int N, int K) {
 // cover K exactly use straight-line loads with immediate offsets.  For M >= 6
 // the activation tile of a 5-chunk K-tile alone (M * 10 KiB per block) would
 // cap the CU at two blocks, so those rows take 2-chunk tiles.
-// KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile;
-// from M = 2 a block holds two row sets (eight waves, eight row groups) that
+// KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile
+// at M = 1; a block may hold two row sets (eight waves, eight row groups) that
 // share one staged activation tile, which halves the activation traffic per
-// row (down projection 2560<-10240: M = 2 9.9 -> 9.4 us, M = 3 12.3 -> 11.1 us,
-// M = 5 17.3 -> 16.2 us; at M = 1 one row set is faster, 6.5 vs 6.9 us).
+// row (see Sched<M, 4, CLS> for where that pays).
 // RS: row sets per block (K-split only).
 // KSPLIT 5: one chunk per lane; two rows per lane from M = 2 (in the grouped
 // q/k/v launch, one row per lane doubles the blocks and cost 1.2-2 us per
@@ -65,13 +64,18 @@ struct Sched<M, 1, CLS> {
   static constexpr int DEPTH = (R == 2 && M == 1) ? 3 : 2;
   static constexpr int RS = 1;
 };
+// Long rows (class 1): one row per lane up to M = 5, two from M = 6; two row
+// sets per block only at M = 3 and from M = 6 (same-box A/B on the down
+// projection 2560 <- 10240 with the padded staging, us: M = 2 8.61 -> 8.45,
+// M = 3 10.70 -> 10.28, M = 4 14.25 -> 12.53, M = 5 15.46 -> 14.91, M = 8
+// unchanged; the block count 2560 / (4 R RS) then fills all 256 CUs).
 template <int M, int CLS>
 struct Sched<M, 4, CLS> {
-  static constexpr int R = (CLS == 1 && M >= 3) ? 2 : 1;
+  static constexpr int R = (CLS == 1 && M >= 6) ? 2 : 1;
   static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 ? 2 : 1);
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 2;
-  static constexpr int RS = (CLS == 1 && M >= 2) ? 2 : 1;
+  static constexpr int RS = (CLS == 1 && (M == 3 || M >= 6)) ? 2 : 1;
 };
 template <int M, int CLS>
 struct Sched<M, 5, CLS> {

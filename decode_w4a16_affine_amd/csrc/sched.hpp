@@ -43,7 +43,7 @@ inline int ksplit_for(int N, int K) {
 // RS: row sets per block (K-split only).
 // KSPLIT 5: one chunk per lane; two rows per lane from M = 2 (in the grouped
 // q/k/v launch, one row per lane doubles the blocks and cost 1.2-2 us per
-// launch at M = 2..5).
+// launch at M = 2..5); class 1 (N > 2048) takes four from M = 6.
 // PRE: chunk slots whose loads go out before the activations are staged (the
 // rest follow the staging barrier, so the activation loads are not queued
 // behind the whole tile).  DEPTH: chunk slots in flight per lane; later slots
@@ -77,9 +77,16 @@ struct Sched<M, 4, CLS> {
   static constexpr int DEPTH = 2;
   static constexpr int RS = (CLS == 1 && (M == 3 || M >= 6)) ? 2 : 1;
 };
+// Class 1: N > 2048.  From M = 6 those rows take four rows per lane: at M = 8
+// the staged activation tile (about 84 KiB) leaves room for one block per CU,
+// and 2560 rows at two rows per lane make 320 blocks, two generations on 256
+// CUs; four rows per lane make 160, one generation (same-box A/B on the q/k/v
+// launch 2560 + 2 x 512 <- 2560, us: M = 6 9.18 -> 8.90, M = 7 10.39 -> 9.92,
+// M = 8 13.13 -> 11.22).  Narrow matrices keep two rows per lane: on their own
+// four would halve an already small grid (512 rows: 5.4 -> 8.3 us at M = 6).
 template <int M, int CLS>
 struct Sched<M, 5, CLS> {
-  static constexpr int R = M == 1 ? 1 : 2;
+  static constexpr int R = M == 1 ? 1 : (CLS == 1 && M >= 6) ? 4 : 2;
   static constexpr int CPL = 1;
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 1;
@@ -117,7 +124,7 @@ struct LmSched : Sched<M, KSPLIT, CLS> {
 constexpr int kRoutedPassRows = 2;
 
 inline int sched_class(int N, int K, int ksplit) {
-  if (ksplit == 5) return 0;
+  if (ksplit == 5) return N > 2048;
   if (ksplit == 4) return K > 4096;
   return (N >= 131072 ? 1 : 0) | (K % 2048 != 0 && K % 2560 == 0 ? 2 : 0) | (N >= 16384 ? 4 : 0);
 }
@@ -126,7 +133,9 @@ inline int sched_class(int N, int K, int ksplit) {
 template <typename F>
 auto with_sched(int ksplit, int cls, F&& f) {
   using std::integral_constant;
-  if (ksplit == 5) return f(integral_constant<int, 5>{}, integral_constant<int, 0>{});
+  if (ksplit == 5)
+    return cls ? f(integral_constant<int, 5>{}, integral_constant<int, 1>{})
+               : f(integral_constant<int, 5>{}, integral_constant<int, 0>{});
   if (ksplit == 4)
     return cls ? f(integral_constant<int, 4>{}, integral_constant<int, 1>{})
                : f(integral_constant<int, 4>{}, integral_constant<int, 0>{});

@@ -102,12 +102,13 @@ def check(orc, fz, x_bits, cols, ref, what):
 # (I, K, group): the decode gate_up layer (2I = 20480, K = 2560); ragged I just
 # above the K-split limit; N = 2I past 16384 with a short K; a vocabulary-sized
 # fused matrix (2I >= 131072); group 128.  K-split form (2I <= 4096): five
-# slices (K = 2560, 5120), four (K = 1024, 640), four with K > 4096 (the
+# slices (K = 2560, 5120; 2I > 2048 takes four rows per lane from M = 6, also
+# with a ragged last block), four (K = 1024, 640), four with K > 4096 (the
 # class with two rows per lane from M = 3), and I below one block's rows.
 CASES = [(10240, 2560, 64), (2049, 640, 64), (8195, 576, 64), (65600, 256, 64), (2100, 1280, 128),
          (3000, 5120, 128),
-         (2048, 2560, 64), (700, 5120, 128), (1000, 1024, 64), (37, 640, 128), (1500, 6144, 64), (1, 2560, 64),
-         (5, 1024, 64)]
+         (2048, 2560, 64), (1100, 2560, 64), (700, 5120, 128), (1000, 1024, 64), (37, 640, 128), (1500, 6144, 64),
+         (1, 2560, 64), (5, 1024, 64)]
 
 
 @pytest.mark.parametrize("I,K,G", CASES)

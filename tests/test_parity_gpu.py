@@ -158,7 +158,7 @@ def test_decode_projections_and_verify_batches(orc, name):
 # rows per lane and the tile length change with M; (1003, 6208): a K-split row
 # whose blocks hold two row sets from M = 2, with a ragged last block
 RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560), (61, 2560), (300, 5120),
-          (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560), (1003, 6208)]
+          (2049, 5120), (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560), (1003, 6208)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)
@@ -432,6 +432,29 @@ def test_lmhead_ties_and_planted_maximum(orc, N):
     assert int(am[1]) == int(np.flatnonzero(y[1] == y[1].max())[0])
 
 
+# K-split LM heads (N <= 4096) at every M, including the wide five-way split
+# whose rows go four per lane from M = 6 and a ragged last block.
+@pytest.mark.parametrize("N,K", [(3001, 2560), (700, 5120), (2500, 1024)])
+def test_lmhead_k_split_every_M(orc, N, K):
+    w = synthetic.quantized_weights(N, K, seed=N + K, tag=(5,), bias="exact")
+    x = synthetic.activations(8, K, seed=N + K, tag=(5,))
+    say(f"lm head K-split N={N} K={K}: oracle (all rows, M=8)")
+    y64, absy = oracle_qmm(orc, x, w)
+    dw = DevWeights(w)
+    for M in range(1, 9):
+        say(f"  lm head N={N} K={K} M={M}")
+        xd = dev_bf16(x[:M])
+        am, logits = w4.lmhead_argmax(xd, dw.qw, dw.s, dw.b, out_dtype=torch.float32)
+        ym = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        w4.w4a16_matmul(xd, dw.qw, dw.s, dw.b, ym)
+        torch.cuda.synchronize()
+        y32, am = host_f32(logits), am.cpu().numpy()
+        check_f32(y32, y64[:M], absy[:M], f"lm head N={N} K={K} M={M}")
+        assert np.array_equal(host_f32(ym).view(np.uint32), y32.view(np.uint32))
+        for m in range(M):
+            assert am[m] == int(np.flatnonzero(y32[m] == y32[m].max())[0]), (N, K, M, m)
+
+
 # ---------------------------------------------------------------------------
 # Routed (expert-gathered) product
 # ---------------------------------------------------------------------------
@@ -546,7 +569,7 @@ def run_mm_g(dw, x_bits, N, group, f32=False):
 # one case per schedule class: tiny, one-chunk K-split, long-row K-split (two
 # row sets from M = 2), one row group per row, several K-tiles (double
 # buffered at M = 1), N >= 16384 with K % 2560 == 0
-G128 = [(8, 128), (300, 2560), (1003, 6272), (4097, 768), (4200, 5120), (16400, 2560)]
+G128 = [(8, 128), (300, 2560), (3001, 2560), (1003, 6272), (4097, 768), (4200, 5120), (16400, 2560)]
 
 
 @pytest.mark.parametrize("N,K", G128)

@@ -378,6 +378,13 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
 // buffers stay within 32 KiB per block, i.e. four blocks still fit on a CU.
 template <int M, int CPL, int KSPLIT>
 constexpr bool kRolled = KSPLIT == 1 && 2 * M * 8 * CPL * kRowLanes * 16 <= 32768;
+// Rows of two or more one-chunk tiles with a four-way K-split (the down
+// projection from M = 4) take paired_tiles.  The path's registers count against
+// every kernel it is compiled into, so schedules whose rows usually fit one
+// tile (K-split 5: K = 2560) or that measured slower with it (two-chunk tiles,
+// +12-16% at M = 2, 3) keep the tile-by-tile walk.
+template <int M, int CPL, int KSPLIT>
+constexpr bool kPaired = KSPLIT == 4 && CPL == 1;
 // float4 of LDS a block needs for its activation tiles
 template <int M, int CPL, int KSPLIT, bool PAD = kPadDefault<M, KSPLIT>>
 constexpr int kXsF4 = M * 8 * kPieceStride<CPL * kRowLanes * KSPLIT, PAD> * (kRolled<M, CPL, KSPLIT> ? 2 : 1);
@@ -477,6 +484,114 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
   }
 }
 
+// Rows of two or more full K-tiles whose activation tile cannot be doubled in
+// LDS (the K-split schedules, whose tiles span KSPLIT waves of lanes), walked
+// with the next tile's weights in flight: two register sets hold the chunk
+// slots of tiles t and t + 1; consuming slot j of tile t issues slot j of tile
+// t + 2 into the same registers, so between CPL and 2 CPL slots per lane are
+// always in flight, also across the staging barriers.  The next tile's
+// activations are loaded into registers during the current tile and written
+// into the one LDS buffer between two barriers.  Loads past the last tile use
+// an out-of-range offset (no traffic, no branch around the load).  Each lane
+// consumes its chunks in the same order with the same body as tile_pass: the
+// sums are bitwise those of the tile-by-tile walk.  xs holds one tile
+// (kXsF4 float4).
+template <int M, int R, int CPL, int KSPLIT, int RS, int G, bool PAD, bool NTLOAD>
+__device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>& xr, const WaveRows& w,
+                                             int ntiles, float4* xs) {
+  constexpr int LPR = kRowLanes * KSPLIT;
+  constexpr int CS = CPL * LPR;                               // chunks per K-tile
+  constexpr int KTILE = CS * 32;                              // codes per K-tile
+  constexpr int NT = kBlockThreads<KSPLIT, RS>;
+  constexpr int XQ = KTILE / 8;                               // 16-byte x pieces per row per tile
+  constexpr int XL = (XQ + NT - 1) / NT;
+  constexpr int PS = kPieceStride<CS, PAD>;
+  const int L = w.L;
+
+  uint4 xv[M][XL];
+  auto x_issue = [&](int t) {
+    const int tt = min(t, ntiles - 1);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        const int i = min((int)threadIdx.x + j * NT, XQ - 1);
+        xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + tt * KTILE)[i];
+      }
+  };
+
+  // byte offsets of chunk slot 0 of the tile each register set loads next
+  uint32_t qa[R], ga[R], qb[R], gb[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t lr = (uint32_t)(w.slot * R + r);
+    qa[r] = lr * w.wpr * 4u + (uint32_t)L * 16u;
+    ga[r] = lr * w.gpr * 2u + (uint32_t)L / kChunksPerGroup<G> * 2u;
+    qb[r] = qa[r] + (uint32_t)CS * 16u;
+    gb[r] = ga[r] + (uint32_t)(CS / kChunksPerGroup<G>) * 2u;
+  }
+  auto load = [&](Tile<CPL, R>& tl, const uint32_t (&q0)[R], const uint32_t (&g0)[R], int j, bool live) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t oq = live ? q0[r] + (uint32_t)(j * LPR * 16) : kOffNone;
+      const uint32_t og = live ? g0[r] + (uint32_t)(j * LPR / kChunksPerGroup<G>) * 2u : kOffNone;
+      tl.w[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w.rq, oq, 0, NTLOAD ? 2 : 0));
+      tl.s[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, og, 0, 0);
+      tl.b[j][r] = __builtin_amdgcn_raw_buffer_load_b16(w.rb, og, 0, 0);
+    }
+  };
+  auto advance2 = [&](uint32_t (&q0)[R], uint32_t (&g0)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      q0[r] += (uint32_t)(2 * CS) * 16u;
+      g0[r] += (uint32_t)(2 * CS / kChunksPerGroup<G>) * 2u;
+    }
+  };
+  auto stage = [&]() {
+    __syncthreads();   // every wave is done reading the current tile
+    x_stage_tile<M, XL, NT, PS>(xv, XQ, xs);
+    __syncthreads();
+  };
+
+  Tile<CPL, R> ta, tb;
+  x_issue(0);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) load(ta, qa, ga, j, true);
+  advance2(qa, ga);
+  __syncthreads();   // the block is done with any earlier contents of xs
+  x_stage_tile<M, XL, NT, PS>(xv, XQ, xs);
+  x_issue(1);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) load(tb, qb, gb, j, true);
+  advance2(qb, gb);
+  __syncthreads();
+
+  int t = 0;
+  for (; t + 2 <= ntiles; t += 2) {
+    const bool live_a = t + 2 < ntiles, live_b = t + 3 < ntiles;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      consume_slot<M, R, PS>(acc, ta, j, xs + L + j * LPR);
+      load(ta, qa, ga, j, live_a);
+    }
+    advance2(qa, ga);
+    stage();                  // tile t + 1
+    x_issue(t + 2);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      consume_slot<M, R, PS>(acc, tb, j, xs + L + j * LPR);
+      load(tb, qb, gb, j, live_b);
+    }
+    advance2(qb, gb);
+    if (live_a) stage();      // tile t + 2
+    x_issue(t + 3);
+  }
+  if (t < ntiles) {           // an odd count: the last tile is in ta, staged
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) consume_slot<M, R, PS>(acc, ta, j, xs + L + j * LPR);
+  }
+}
+
 // Full-row sums for the R rows of this lane's row group.
 //
 // Lane L of a row (L = t without K-split, wave*16 + t with one) owns the
@@ -526,6 +641,12 @@ __device__ __forceinline__ void block_rows(float (&acc)[R][M], const XRows<M>& x
     const int nfull = K / KTILE;
     if (nfull >= 2) {
       rolled_tiles<M, R, CPL, PRE, DEPTH, G, PAD, NTLOAD>(acc, xr, w, nfull, xs);
+      kr = nfull * KTILE;
+    }
+  } else if constexpr (kPaired<M, CPL, KSPLIT>) {
+    const int nfull = K / KTILE;
+    if (nfull >= 2) {
+      paired_tiles<M, R, CPL, KSPLIT, RS, G, PAD, NTLOAD>(acc, xr, w, nfull, xs);
       kr = nfull * KTILE;
     }
   }

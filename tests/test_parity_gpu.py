@@ -158,7 +158,8 @@ def test_decode_projections_and_verify_batches(orc, name):
 # rows per lane and the tile length change with M; (1003, 6208): a K-split row
 # whose blocks hold two row sets from M = 2, with a ragged last block
 RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560), (61, 2560), (300, 5120),
-          (2049, 5120), (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560), (1003, 6208)]
+          (2049, 5120), (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560), (1003, 6208), (1000, 4096),
+          (77, 8256)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)
@@ -433,8 +434,9 @@ def test_lmhead_ties_and_planted_maximum(orc, N):
 
 
 # K-split LM heads (N <= 4096) at every M, including the wide five-way split
-# whose rows go four per lane from M = 6 and a ragged last block.
-@pytest.mark.parametrize("N,K", [(3001, 2560), (700, 5120), (2500, 1024)])
+# whose rows go four per lane from M = 6 and a ragged last block, and four-way
+# splits whose rows span several one-chunk tiles (with and without a ragged one).
+@pytest.mark.parametrize("N,K", [(3001, 2560), (700, 5120), (2500, 1024), (1200, 6208), (900, 4096)])
 def test_lmhead_k_split_every_M(orc, N, K):
     w = synthetic.quantized_weights(N, K, seed=N + K, tag=(5,), bias="exact")
     x = synthetic.activations(8, K, seed=N + K, tag=(5,))
@@ -502,13 +504,15 @@ def test_routed_moe_config(orc):
         assert np.array_equal(host_f32(yd)[0].view(np.uint32), y8[m, j].view(np.uint32))
 
 
-def test_routed_long_rows(orc):
+@pytest.mark.parametrize("E,N,K", [(3, 4100, 4288), (2, 600, 6208)])
+def test_routed_long_rows(orc, E, N, K):
     # experts tall enough for one row group per row and K spanning two full
-    # K-tiles plus a ragged tail
-    E, N, K, M, top_k = 3, 4100, 4288, 3, 2
+    # K-tiles plus a ragged tail; short experts with a four-way K-split whose
+    # rows span three one-chunk tiles plus a ragged tail
+    M, top_k = 3, 2
     w, x, _ = routed_inputs(E, N, K, M, top_k, seed=21)
     stack = (dev_qw(w.qw), dev_bf16(w.scales), dev_bf16(w.biases))
-    ids = np.array([[0, 2], [1, 0], [2, 1]], dtype=np.int32)
+    ids = np.array([[0, 2], [1, 0], [2, 1]] if E == 3 else [[0, 1], [1, 0], [0, 1]], dtype=np.int32)
     say(f"routed long rows E={E} N={N} K={K} M={M}: oracle")
     y64, absy = orc.qmm_id(x, w.qw, w.scales, w.biases, ids)
     y = run_id(stack, x, ids, N)

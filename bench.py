@@ -35,6 +35,10 @@ import synthetic  # noqa: E402
 METRIC = "achieved HBM GB/s (% of MI355X peak) for W4A16 qmv M=1 and qmm M=k+1"
 PEAK_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
+# fp32 fma rate without packed instructions (256 CUs x 4 SIMDs x 16 lanes x 2
+# flops x 2.4 GHz; the packed form that doubles it is not used by the build,
+# and a probe measured 4.25 cycles per wave64 fma per SIMD at that clock).
+PEAK_FP32_FMA_TFLOPS = 78.6
 PREFILL_M = (16, 64, 512, 4096)
 LAYERS = 42
 # untimed replay time before each measurement (beyond the warm-up count): the
@@ -125,6 +129,16 @@ def make_step(w4, stack, M: int, layers: int, units=UNITS_GROUPED, only=None):
 
 def unit_bytes(M: int, ps) -> int:
     return sum(call_bytes(M, *synthetic.PROJECTIONS[p]) for p in ps)
+
+
+def unit_flops(M: int, ps) -> int:
+    # per weight: the dequantizing fma, then one fma per activation row
+    return sum(2 * (M + 1) * synthetic.PROJECTIONS[p][0] * synthetic.PROJECTIONS[p][1] for p in ps)
+
+
+def step_fp32_floor_ms(M: int, layers: int) -> float:
+    """The step's fp32 fmas at PEAK_FP32_FMA_TFLOPS (no launch or memory time)."""
+    return layers * sum(unit_flops(M, ps) for _, ps in UNITS_GROUPED) / (PEAK_FP32_FMA_TFLOPS * 1e12) * 1e3
 
 
 def capture(torch, fn):
@@ -584,6 +598,9 @@ def main():
         d = kernel_durations(torch, w4, stack, L, M=M)
         verify_units[M] = {u: dict(us=round(v, 3), gbs=round(unit_bytes(M, unit_ps[u]) / (v * 1e-6) / 1e9, 1),
                                    frac_of_peak=round(unit_bytes(M, unit_ps[u]) / (v * 1e-6) / 1e9 / PEAK_GBS, 4),
+                                   fp32_tflops=round(unit_flops(M, unit_ps[u]) / (v * 1e-6) / 1e12, 2),
+                                   frac_of_fp32_fma_peak=round(unit_flops(M, unit_ps[u]) / (v * 1e-6) / 1e12
+                                                               / PEAK_FP32_FMA_TFLOPS, 4),
                                    kernel=w4.w4a16_schedule_name(M, *synthetic.PROJECTIONS[unit_ps[u][0]]))
                            for u, v in d.items()}
         log(f"M={M} launches (us): " + ", ".join(f"{u} {v['us']}" for u, v in verify_units[M].items()))
@@ -641,6 +658,9 @@ def main():
         "verify": {str(M): dict(gbs=round(r["gbs"], 2), ms_per_step=round(r["ms"], 5),
                                 frac_of_peak=round(r["gbs"] / PEAK_GBS, 4),
                                 cost_vs_m1=round(r["ms"] / r1["ms"], 4), ms_per_step_pct=r["pct"],
+                                fp32_fma_floor_ms=round(step_fp32_floor_ms(M, L), 5),
+                                hbm_floor_ms=round(r["bytes"] / (PEAK_GBS * 1e9) * 1e3, 5),
+                                frac_of_fp32_fma_peak=round(step_fp32_floor_ms(M, L) / r["ms"], 4),
                                 per_launch=verify_units.get(M))
                    for M, r in results.items() if M != 1},
         "roofline": roofline,

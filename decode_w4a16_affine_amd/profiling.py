@@ -227,10 +227,17 @@ def traffic_per_launch(record_path: str, kernel: str, grid_sizes_weights: dict):
     return tot / n if n else None
 
 
+# VALU issue time of a launch if every SIMD issued one wave64 instruction per
+# 4 cycles (16 lanes per cycle, the rate a probe measured for fp32 fma) at
+# 2.4 GHz: total VALU instructions / (256 CUs x 4 SIMDs) x 4 cycles.
+VALU_US_PER_INSTR = 4.0 / (256 * 4) / 2400.0
+
+
 def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
     """Per kernel and grid size: median shader-sequencer counts per launch and
     per wave (VALU and LDS instructions, LDS bank-conflict cycles per LDS
-    instruction, wave cycles)."""
+    instruction, wave cycles), and the launch's VALU issue time at one wave
+    instruction per SIMD per 4 cycles."""
     groups = {}
     for path in csv_path.split(","):   # several counter passes of the same program
         for r in csv.DictReader(open(path)):
@@ -240,15 +247,17 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
             groups.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     matrix = any("SQ_INSTS_MFMA" in d for d in groups.values())
     lines = ["# Shader-sequencer counters per launch", "", f"Command: `{command}`", "",
-             "| kernel | grid | waves | VALU instr / wave | LDS instr / wave | LDS conflict cycles / LDS instr | "
+             "| kernel | grid | waves | VALU instr / wave | VALU issue (us, all SIMDs) | LDS instr / wave | "
+             "LDS conflict cycles / LDS instr | "
              "wave cycles / wave |" + (" MFMA instr / wave | MFMA busy / CU busy (per SIMD) | waiting on a dependency "
                                        "/ wave cycles | waiting on LDS / wave cycles |" if matrix else ""),
-             "|---|---|---|---|---|---|---|" + ("---|---|---|---|" if matrix else "")]
+             "|---|---|---|---|---|---|---|---|" + ("---|---|---|---|" if matrix else "")]
     for (k, g), d in sorted(groups.items()):
         med = {c: statistics.median(v) for c, v in d.items()}
         waves = med.get("SQ_WAVES", 0.0) or 1.0
         lds = med.get("SQ_INSTS_LDS", 0.0)
-        line = (f"| `{k}` | {g} | {int(waves)} | {med.get('SQ_INSTS_VALU', 0.0) / waves:.0f} | {lds / waves:.0f} | "
+        line = (f"| `{k}` | {g} | {int(waves)} | {med.get('SQ_INSTS_VALU', 0.0) / waves:.0f} | "
+                f"{med.get('SQ_INSTS_VALU', 0.0) * VALU_US_PER_INSTR:.2f} | {lds / waves:.0f} | "
                 f"{med.get('SQ_LDS_BANK_CONFLICT', 0.0) / max(lds, 1.0):.2f} | "
                 f"{med.get('SQ_WAVE_CYCLES', 0.0) / waves:.0f} |")
         if matrix:

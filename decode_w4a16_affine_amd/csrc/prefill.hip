@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ops.hpp"
 #include "qmm_device.hpp"
 #include "qmm_prefill.hpp"
@@ -37,27 +39,49 @@ hipError_t prefill_large(const uint16_t* x, const uint32_t* qw, const uint16_t* 
     return hipGetLastError();
   }
   // Tiles of 64 activation rows x 32 weight rows per wave; when fewer than
-  // 1024 such tiles exist, the four waves of a block split K of one tile.
-  constexpr int TM = 4, TN = 2;
-  const long tiles = (long)((M + 16 * TM - 1) / (16 * TM)) * ((N + 16 * TN - 1) / (16 * TN));
-  const bool ksplit = tiles < 1024;
-  const int cols = ksplit ? 16 * TN : kPrefillWaves * 16 * TN;
-  const dim3 grid((unsigned)((N + cols - 1) / cols), (unsigned)((M + 16 * TM - 1) / (16 * TM)));
-  if (group == 128) {
-    if (ksplit)
-      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 128>), grid, dim3(kPrefillWaves * kWave), 0, s,
-                         x, qw, scales, biases, y, M, N, K, f32);
-    else
-      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 128>), grid, dim3(kPrefillWaves * kWave), 0, s, x, qw,
-                         scales, biases, y, M, N, K, f32);
-  } else {
-    if (ksplit)
-      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 64>), grid, dim3(kPrefillWaves * kWave), 0, s,
-                         x, qw, scales, biases, y, M, N, K, f32);
-    else
-      hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 64>), grid, dim3(kPrefillWaves * kWave), 0, s, x, qw,
-                         scales, biases, y, M, N, K, f32);
-  }
+  // 1024 such tiles exist, the four waves of a block split K of one tile and
+  // the grid is one block per tile.  Such a grid then takes the smallest of
+  // the 32 x 16, 32 x 32 and 64 x 32 tiles whose blocks fit one per CU (256
+  // on MI355X), else 64 x 32: a grid just above the CU count runs in two
+  // rounds.  Same-box A/B on the down projection 2560 <- 10240 (us, 64 x 32
+  // tiles -> chosen): M = 24 76.3 -> 43.6 (32 x 16), M = 32 80.4 -> 47.7
+  // (32 x 16), M = 48 87.6 -> 72.7, M = 64 95.4 -> 74.5, M = 96 91.2 -> 74.0
+  // (32 x 32); from M = 128 unchanged (64 x 32; 32 x 32 tiles there made 320
+  // blocks, 94 -> 141).  The tile shape does not change any sum's order.
+  constexpr long kCUs = 256;
+  auto tiles_of = [&](int tm, int tn) {
+    return (long)((M + 16 * tm - 1) / (16 * tm)) * ((N + 16 * tn - 1) / (16 * tn));
+  };
+  const bool ksplit = tiles_of(4, 2) < 1024;
+  const int shape = !ksplit ? 0 : tiles_of(2, 1) <= kCUs ? 1 : tiles_of(2, 2) <= kCUs ? 2 : 0;
+  auto launch = [&](auto tm_c, auto tn_c) {
+    constexpr int TM = decltype(tm_c)::value, TN = decltype(tn_c)::value;
+    const int cols = ksplit ? 16 * TN : kPrefillWaves * 16 * TN;
+    const dim3 grid((unsigned)((N + cols - 1) / cols), (unsigned)((M + 16 * TM - 1) / (16 * TM)));
+    const dim3 block(kPrefillWaves * kWave);
+    if (group == 128) {
+      if (ksplit)
+        hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 128>), grid, block, 0, s, x, qw, scales, biases,
+                           y, M, N, K, f32);
+      else
+        hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 128>), grid, block, 0, s, x, qw, scales, biases, y, M, N, K,
+                           f32);
+    } else {
+      if (ksplit)
+        hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, kPrefillWaves, 64>), grid, block, 0, s, x, qw, scales, biases,
+                           y, M, N, K, f32);
+      else
+        hipLaunchKernelGGL((qmm_prefill_kernel<TM, TN, 1, 64>), grid, block, 0, s, x, qw, scales, biases, y, M, N, K,
+                           f32);
+    }
+  };
+  using std::integral_constant;
+  if (shape == 1)
+    launch(integral_constant<int, 2>{}, integral_constant<int, 1>{});
+  else if (shape == 2)
+    launch(integral_constant<int, 2>{}, integral_constant<int, 2>{});
+  else
+    launch(integral_constant<int, 4>{}, integral_constant<int, 2>{});
   return hipGetLastError();
 }
 

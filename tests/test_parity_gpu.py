@@ -651,11 +651,14 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
 # splitting K (257 x 4097, 520 x 2560, 300 x 3000 at G = 128, 200 x 8000 with
 # an odd number of K steps, and 40 x 9000 with one partial row tile); the
 # other shapes run the per-wave form (31 x 9000 and 20 x 2560 <- 10240: long
-# K walks with three steps of loads in flight).
+# K walks with three steps of loads in flight) in 64 x 32 tiles, or in 32 x 16
+# tiles (33 x 300, 100 x 1000, 70 x 513, 64 x 128, 20 x 2560) or 32 x 32 tiles
+# (90 x 2600, ragged in both) where those keep the grid within one block per CU.
 PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 4097, 1024, 64), (64, 128, 64, 64),
            (70, 513, 1280, 128), (1, 77, 256, 128), (520, 2560, 2560, 64), (300, 12837, 640, 128),
            (520, 16390, 512, 64), (256, 32768, 256, 64), (300, 3000, 640, 128), (200, 8000, 704, 64),
-           (40, 9000, 640, 64), (100, 32768, 256, 128), (31, 9000, 2560, 64), (20, 2560, 10240, 64)]
+           (40, 9000, 640, 64), (100, 32768, 256, 128), (31, 9000, 2560, 64), (20, 2560, 10240, 64),
+           (90, 2600, 1024, 128)]
 
 
 @pytest.mark.parametrize("M,N,K,G", PREFILL)

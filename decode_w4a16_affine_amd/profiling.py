@@ -266,6 +266,19 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
                      f"{med.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / 4 / max(med.get('SQ_BUSY_CU_CYCLES', 0.0), 1.0):.2f} | "
                      f"{med.get('SQ_WAIT_INST_ANY', 0.0) / wc:.2f} | {med.get('SQ_WAIT_INST_LDS', 0.0) / wc:.2f} |")
         lines.append(line)
+    # memory waiting and vector-memory instructions in flight, where a pass
+    # collected them (SQ_INST_LEVEL_VMEM accumulates the outstanding count
+    # every cycle, so divided by the wave cycles it is the average in flight)
+    extra = [(k, g, d) for (k, g), d in sorted(groups.items()) if "SQ_WAIT_ANY" in d and "SQ_INST_LEVEL_VMEM" in d]
+    if extra:
+        lines += ["", "| kernel | grid | waiting (any) / wave cycles | vector-memory reads / wave | "
+                      "vector-memory instructions in flight (average) |", "|---|---|---|---|---|"]
+        for k, g, d in extra:
+            med = {c: statistics.median(v) for c, v in d.items()}
+            wc = max(med.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+            waves = med.get("SQ_WAVES", 0.0) or 1.0
+            lines.append(f"| `{k}` | {g} | {med['SQ_WAIT_ANY'] / wc:.2f} | "
+                         f"{med.get('SQ_INSTS_VMEM_RD', 0.0) / waves:.0f} | {med['SQ_INST_LEVEL_VMEM'] / wc:.2f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 

@@ -48,6 +48,7 @@ __device__ __forceinline__ void store_to(const float (&acc)[R][M], int row_first
 // kernel-argument load each.
 constexpr int kMaxMats = 8;
 static_assert(kMaxMats >= W4A16_MAX_GROUP, "a grouped launch must hold every matrix of a call");
+constexpr long kDenseCUs = 256;   // compute units of MI355X (one block per CU per round)
 struct MatDesc {
   const uint32_t* qw;
   const uint16_t* scales;
@@ -67,10 +68,15 @@ struct MatArgs {
   int N[kMaxMats - 1];
 };
 
+// split: with two rows per lane and no K-split, blocks from `split` on take
+// one row per lane (16-row blocks after the first split * 32 rows), so that a
+// grid of 2.5 blocks per CU becomes two large and one small block per CU and
+// no SIMD holds three waves of the large kind while others hold two.  Rows per
+// lane never change a row's arithmetic.
 template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS, int G>
 __global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
     const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
-    int N0, int K, int out_f32, const MatArgs more) {
+    int N0, int K, int out_f32, const MatArgs more, int split) {
   __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
   __shared__ float red[kBlockWaves<KSPLIT, RS> * kSlots * R * M];
   using RM = RowMap<R, KSPLIT, RS>;
@@ -79,8 +85,6 @@ __global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
     const int mi = blockIdx.y - 1;
     d = MatDesc{more.qw[mi], more.scales[mi], more.biases[mi], more.y[mi], more.N[mi]};
   }
-  const int block_row0 = (int)blockIdx.x * RM::kRowsPerBlock;
-  if (block_row0 >= d.N) return;   // uniform per block: before any barrier
   XRows<M> xr;
   size_t yoff[M];
 #pragma unroll
@@ -89,6 +93,19 @@ __global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
     yoff[m] = (size_t)m * d.N;
   }
   const RowSrc src{d.qw, d.scales, d.biases, d.N, K};
+  if constexpr (KSPLIT == 1 && R == 2 && RS == 1) {
+    if ((int)blockIdx.x >= split) {
+      using RM1 = RowMap<1, 1, 1>;
+      const int block_row0 = split * RM::kRowsPerBlock + ((int)blockIdx.x - split) * RM1::kRowsPerBlock;
+      if (block_row0 >= d.N) return;   // uniform per block: before any barrier
+      float acc1[1][M];
+      block_rows<M, 1, CPL, 1, PRE, DEPTH, 1, G>(acc1, xr, src, block_row0, xs, red);
+      store_to<M, 1, 1, 1>(acc1, RM1::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
+      return;
+    }
+  }
+  const int block_row0 = (int)blockIdx.x * RM::kRowsPerBlock;
+  if (block_row0 >= d.N) return;   // uniform per block: before any barrier
   float acc[R][M];
   block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>(acc, xr, src, block_row0, xs, red);
   store_to<M, R, KSPLIT, RS>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
@@ -400,10 +417,23 @@ hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, 
     a.y[i - 1] = ml.m[i].y;
     a.N[i - 1] = ml.m[i].N;
   }
+  // one matrix with two rows per lane and a grid that is not a whole number of
+  // rounds over the CUs: the blocks after the last whole round split into
+  // one-row-per-lane blocks, if those fit one per CU
+  long split = blocks;
+  if (KSPLIT == 1 && R == 2 && RS == 1 && ml.count == 1 && blocks > kDenseCUs && blocks % kDenseCUs) {
+    const long big = blocks / kDenseCUs * kDenseCUs;
+    const long small = (ml.m[0].N - big * RM::kRowsPerBlock + kSlots * kWaves - 1) / (kSlots * kWaves);
+    if (small <= kDenseCUs) {
+      split = big;
+      blocks = big + small;
+    }
+  }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const MatDesc& m0 = ml.m[0];
   hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>), dim3((unsigned)blocks, (unsigned)ml.count),
-                     dim3((kBlockThreads<KSPLIT, RS>)), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a);
+                     dim3((kBlockThreads<KSPLIT, RS>)), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a,
+                     (int)split);
   return hipGetLastError();
 }
 

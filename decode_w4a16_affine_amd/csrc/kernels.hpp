@@ -185,19 +185,15 @@ __global__ __launch_bounds__(kBlockThreads<KSPLIT>) void qmm_lmhead_kernel(const
 // matrix; the up sums reach the gate waves through LDS, which write
 // h = GELU(gate) * up, GELU(g) = g * Phi(g) = 0.5 g (1 + erf(g / sqrt 2)), in
 // fp32, rounded once.  Only for matrices without a K-split (2I > 4096).
+// One block's rows [j0, j0 + kHalf) of the gate and up halves, kHalf = 8R.
 template <int M, int R, int CPL, int PRE, int DEPTH, int G>
-__global__ __launch_bounds__(kBlockThreads<1>) void qmm_geglu_kernel(const uint16_t* __restrict__ x,
-                                                                     const uint32_t* qw, const uint16_t* scales,
-                                                                     const uint16_t* biases, void* h, int I, int K,
-                                                                     int out_f32) {
-  __shared__ float4 xs[kXsF4<M, CPL, 1>];
-  __shared__ float red[kBlockWaves<1> * kSlots * R * M];
-  __shared__ float ups[2 * kSlots * R * M];
+__device__ __forceinline__ void geglu_rows(const uint16_t* __restrict__ x, const uint32_t* qw, const uint16_t* scales,
+                                           const uint16_t* biases, void* h, int I, int K, int out_f32, int j0,
+                                           float4* xs, float* red, float* ups) {
   constexpr int kHalf = 2 * kSlots * R;          // gate (and up) rows per block
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane & (kRowLanes - 1), slot = lane / kRowLanes;
-  const int j0 = (int)blockIdx.x * kHalf;
   XRows<M> xr;
 #pragma unroll
   for (int m = 0; m < M; ++m) xr.p[m] = x + (size_t)m * K;
@@ -240,6 +236,27 @@ __global__ __launch_bounds__(kBlockThreads<1>) void qmm_geglu_kernel(const uint1
         reinterpret_cast<uint16_t*>(h)[o] = (uint16_t)f32_to_bf16(v);
     }
   }
+}
+
+// split: with two rows per lane, blocks from `split` on take one row per lane
+// (8 gate and 8 up rows after the first split * 16), as in qmm_dense_kernel.
+template <int M, int R, int CPL, int PRE, int DEPTH, int G>
+__global__ __launch_bounds__(kBlockThreads<1>) void qmm_geglu_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint32_t* qw, const uint16_t* scales,
+                                                                     const uint16_t* biases, void* h, int I, int K,
+                                                                     int out_f32, int split) {
+  __shared__ float4 xs[kXsF4<M, CPL, 1>];
+  __shared__ float red[kBlockWaves<1> * kSlots * R * M];
+  __shared__ float ups[2 * kSlots * R * M];
+  if constexpr (R == 2) {
+    if ((int)blockIdx.x >= split) {
+      geglu_rows<M, 1, CPL, PRE, DEPTH, G>(x, qw, scales, biases, h, I, K, out_f32,
+                                           split * 4 * kSlots + ((int)blockIdx.x - split) * 2 * kSlots, xs, red, ups);
+      return;
+    }
+  }
+  geglu_rows<M, R, CPL, PRE, DEPTH, G>(x, qw, scales, biases, h, I, K, out_f32, (int)blockIdx.x * 2 * kSlots * R, xs,
+                                       red, ups);
 }
 
 // GeGLU for matrices the dense product splits along K (2I <= 4096): a block of
@@ -450,10 +467,19 @@ hipError_t launch_geglu(const uint16_t* x, const uint32_t* qw, const uint16_t* s
   constexpr int kHalf = 2 * kSlots * S::R;
   // the up waves view the matrix from row I - kHalf (implied by 2I > 4096)
   if (I < kHalf) return hipErrorInvalidValue;
-  const long blocks = ((long)I + kHalf - 1) / kHalf;
+  long blocks = ((long)I + kHalf - 1) / kHalf;
+  long split = blocks;
+  if (S::R == 2 && blocks > kDenseCUs && blocks % kDenseCUs) {   // as in launch_dense_list
+    const long big = blocks / kDenseCUs * kDenseCUs;
+    const long small = (I - big * kHalf + kHalf / 2 - 1) / (kHalf / 2);
+    if (small <= kDenseCUs) {
+      split = big;
+      blocks = big + small;
+    }
+  }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((qmm_geglu_kernel<M, S::R, S::CPL, S::PRE, S::DEPTH, G>), dim3((unsigned)blocks),
-                     dim3(kBlockThreads<1>), 0, st, x, qw, s, b, h, I, K, out_f32);
+                     dim3(kBlockThreads<1>), 0, st, x, qw, s, b, h, I, K, out_f32, (int)split);
   return hipGetLastError();
 }
 

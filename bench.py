@@ -67,16 +67,18 @@ def launch_grid(kernel: str, Ns) -> int:
     Ns rows sharing one launch: a grid of (blocks of the tallest matrix) x
     (matrices) blocks; a block is 4 waves holding 16 row groups of R rows, or,
     with a K-split of S, RS row sets of S waves sharing 4 row groups of R rows.
-    One matrix at two rows per lane without a K-split whose blocks are not a
-    whole number of rounds over the CUs ends in one-row-per-lane blocks of 16
-    rows after the last whole round, if those fit one per CU."""
+    One matrix at two rows per lane and one row set whose blocks are not a
+    whole number of rounds over the CUs ends in one-row-per-lane blocks (16
+    rows, or 4 with a K-split) after the last whole round, if those fit one
+    per CU."""
     M, R, CPL, KS, PRE, DEPTH, RS = (int(v) for v in kernel[kernel.index("<") + 1:kernel.index(">")].split(",")[:7])
     rows = (16 if KS == 1 else 4 * RS) * R
     threads = 64 * (4 if KS == 1 else KS * RS)
     blocks = -(-max(Ns) // rows)
-    if KS == 1 and R == 2 and RS == 1 and len(Ns) == 1 and blocks > CUS and blocks % CUS:
+    if R == 2 and RS == 1 and len(Ns) == 1 and blocks > CUS and blocks % CUS:
         big = blocks // CUS * CUS
-        small = -(-(Ns[0] - big * rows) // 16)
+        tail_rows = 16 if KS == 1 else 4
+        small = -(-(Ns[0] - big * rows) // tail_rows)
         if small <= CUS:
             blocks = big + small
     return blocks * len(Ns) * threads

@@ -68,23 +68,23 @@ struct MatArgs {
   int N[kMaxMats - 1];
 };
 
-// split: with two rows per lane and no K-split, blocks from `split` on take
-// one row per lane (16-row blocks after the first split * 32 rows), so that a
-// grid of 2.5 blocks per CU becomes two large and one small block per CU and
-// no SIMD holds three waves of the large kind while others hold two.  Rows per
-// lane never change a row's arithmetic.
-template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS, int G>
-__global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
-    const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
-    int N0, int K, int out_f32, const MatArgs more, int split) {
-  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
-  __shared__ float red[kBlockWaves<KSPLIT, RS> * kSlots * R * M];
-  using RM = RowMap<R, KSPLIT, RS>;
+// The matrix of this grid row (blockIdx.y) and its activation rows.
+template <int M>
+__device__ __forceinline__ MatDesc grid_matrix(const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0,
+                                               void* y0, int N0, const MatArgs& more) {
   MatDesc d{qw0, scales0, biases0, y0, N0};
   if (blockIdx.y > 0) {
     const int mi = blockIdx.y - 1;
     d = MatDesc{more.qw[mi], more.scales[mi], more.biases[mi], more.y[mi], more.N[mi]};
   }
+  return d;
+}
+
+// Rows [block_row0, ...) of one block with the schedule (R, KSPLIT, RS).
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS, int G>
+__device__ __forceinline__ void dense_rows(const uint16_t* __restrict__ x, const MatDesc& d, int K, int out_f32,
+                                           int block_row0, float4* xs, float* red) {
+  using RM = RowMap<R, KSPLIT, RS>;
   XRows<M> xr;
   size_t yoff[M];
 #pragma unroll
@@ -93,22 +93,47 @@ __global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
     yoff[m] = (size_t)m * d.N;
   }
   const RowSrc src{d.qw, d.scales, d.biases, d.N, K};
-  if constexpr (KSPLIT == 1 && R == 2 && RS == 1) {
-    if ((int)blockIdx.x >= split) {
-      using RM1 = RowMap<1, 1, 1>;
-      const int block_row0 = split * RM::kRowsPerBlock + ((int)blockIdx.x - split) * RM1::kRowsPerBlock;
-      if (block_row0 >= d.N) return;   // uniform per block: before any barrier
-      float acc1[1][M];
-      block_rows<M, 1, CPL, 1, PRE, DEPTH, 1, G>(acc1, xr, src, block_row0, xs, red);
-      store_to<M, 1, 1, 1>(acc1, RM1::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
-      return;
-    }
-  }
-  const int block_row0 = (int)blockIdx.x * RM::kRowsPerBlock;
-  if (block_row0 >= d.N) return;   // uniform per block: before any barrier
   float acc[R][M];
   block_rows<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>(acc, xr, src, block_row0, xs, red);
   store_to<M, R, KSPLIT, RS>(acc, RM::first_row(block_row0), d.N, d.y, yoff, out_f32 != 0);
+}
+
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS, int G>
+__global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
+    int N0, int K, int out_f32, const MatArgs more) {
+  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
+  __shared__ float red[kBlockWaves<KSPLIT, RS> * kSlots * R * M];
+  const MatDesc d = grid_matrix<M>(qw0, scales0, biases0, y0, N0, more);
+  const int block_row0 = (int)blockIdx.x * RowMap<R, KSPLIT, RS>::kRowsPerBlock;
+  if (block_row0 >= d.N) return;   // uniform per block: before any barrier
+  dense_rows<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>(x, d, K, out_f32, block_row0, xs, red);
+}
+
+// One matrix at two rows per lane whose grid is not a whole number of rounds
+// over the CUs: blocks from `split` on take one row per lane (rows after the
+// first split blocks), so that a grid of 2.5 blocks per CU becomes two large
+// and one small block per CU and no SIMD holds three waves of the large kind
+// while others hold two.  Rows per lane never change a row's arithmetic.  (A
+// kernel of its own: the second path compiled into qmm_dense_kernel slowed
+// the grouped q/k/v launch that never takes it, +5-12% at M = 2..5.)
+template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int RS, int G>
+__global__ __launch_bounds__((kBlockThreads<KSPLIT, RS>)) void qmm_dense_split_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* qw0, const uint16_t* scales0, const uint16_t* biases0, void* y0,
+    int N0, int K, int out_f32, int split) {
+  static_assert(R == 2 && RS == 1, "splits a two-rows-per-lane grid");
+  __shared__ float4 xs[kXsF4<M, CPL, KSPLIT>];
+  __shared__ float red[kBlockWaves<KSPLIT, RS> * kSlots * R * M];
+  const MatDesc d{qw0, scales0, biases0, y0, N0};
+  if ((int)blockIdx.x >= split) {
+    const int block_row0 = split * RowMap<R, KSPLIT, RS>::kRowsPerBlock +
+                           ((int)blockIdx.x - split) * RowMap<1, KSPLIT, 1>::kRowsPerBlock;
+    if (block_row0 >= d.N) return;   // uniform per block: before any barrier
+    dense_rows<M, 1, CPL, KSPLIT, PRE, DEPTH, 1, G>(x, d, K, out_f32, block_row0, xs, red);
+    return;
+  }
+  dense_rows<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>(x, d, K, out_f32, (int)blockIdx.x * RowMap<R, KSPLIT, RS>::kRowsPerBlock,
+                                                   xs, red);
 }
 
 template <int M, int R, int CPL, int KSPLIT, int PRE, int DEPTH, int G>
@@ -437,20 +462,26 @@ hipError_t launch_dense_list(const uint16_t* x, const MatList& ml, int out_f32, 
   // one matrix with two rows per lane and a grid that is not a whole number of
   // rounds over the CUs: the blocks after the last whole round split into
   // one-row-per-lane blocks, if those fit one per CU
-  long split = blocks;
-  if (KSPLIT == 1 && R == 2 && RS == 1 && ml.count == 1 && blocks > kDenseCUs && blocks % kDenseCUs) {
-    const long big = blocks / kDenseCUs * kDenseCUs;
-    const long small = (ml.m[0].N - big * RM::kRowsPerBlock + kSlots * kWaves - 1) / (kSlots * kWaves);
-    if (small <= kDenseCUs) {
-      split = big;
-      blocks = big + small;
-    }
-  }
   if (blocks > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const MatDesc& m0 = ml.m[0];
+  if constexpr (R == 2 && RS == 1) {
+    // one matrix whose grid is not a whole number of rounds over the CUs:
+    // the blocks after the last whole round split into one-row-per-lane
+    // blocks, if those fit one per CU
+    if (ml.count == 1 && blocks > kDenseCUs && blocks % kDenseCUs) {
+      using RM1 = RowMap<1, KSPLIT, 1>;
+      const long big = blocks / kDenseCUs * kDenseCUs;
+      const long small = (m0.N - big * RM::kRowsPerBlock + RM1::kRowsPerBlock - 1) / RM1::kRowsPerBlock;
+      if (small <= kDenseCUs) {
+        hipLaunchKernelGGL((qmm_dense_split_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>), dim3((unsigned)(big + small)),
+                           dim3((kBlockThreads<KSPLIT, RS>)), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K,
+                           out_f32, (int)big);
+        return hipGetLastError();
+      }
+    }
+  }
   hipLaunchKernelGGL((qmm_dense_kernel<M, R, CPL, KSPLIT, PRE, DEPTH, RS, G>), dim3((unsigned)blocks, (unsigned)ml.count),
-                     dim3((kBlockThreads<KSPLIT, RS>)), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a,
-                     (int)split);
+                     dim3((kBlockThreads<KSPLIT, RS>)), 0, st, x, m0.qw, m0.scales, m0.biases, m0.y, m0.N, K, out_f32, a);
   return hipGetLastError();
 }
 

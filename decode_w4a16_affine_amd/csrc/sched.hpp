@@ -65,7 +65,7 @@ struct Sched<M, 1, CLS> {
   static constexpr int RS = 1;
 };
 // Long rows (class 1): one row per lane up to M = 5, two from M = 6; two row
-// sets per block only at M = 3 and from M = 6 (same-box A/B on the down
+// sets per block only at M = 3 (same-box A/B on the down
 // projection 2560 <- 10240 with the padded staging, us: M = 2 8.61 -> 8.45,
 // M = 3 10.70 -> 10.28, M = 4 14.25 -> 12.53, M = 5 15.46 -> 14.91, M = 8
 // unchanged; the block count 2560 / (4 R RS) then fills all 256 CUs).  From
@@ -73,14 +73,17 @@ struct Sched<M, 1, CLS> {
 // (paired_tiles; same-box A/B, us: M = 2 8.51 -> 8.21 with one-chunk instead
 // of two-chunk tiles, M = 4 12.56 -> 12.27, M = 5 14.92 -> 14.40, M = 7
 // 20.4 -> 18.5, M = 8 20.96 -> 20.61; at M = 3 one-chunk tiles were slower,
-// 10.3 -> 11.5, and two rows per lane at M = 4, 5 too, 12.27 -> 12.67).
+// 10.3 -> 11.5, and two rows per lane at M = 4, 5 too, 12.27 -> 12.67).  From
+// M = 6 one row set per block: 320 blocks, which the split grid turns into 256
+// of 8 rows and 128 of 4 (two row sets gave 160 blocks for 256 CUs; same-box
+// A/B, us: M = 6 16.5 -> 14.0, M = 7 18.5 -> 15.9, M = 8 20.6 -> 17.5).
 template <int M, int CLS>
 struct Sched<M, 4, CLS> {
   static constexpr int R = (CLS == 1 && M >= 6) ? 2 : 1;
   static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 && !(CLS == 1 && M == 2) ? 2 : 1);
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 2;
-  static constexpr int RS = (CLS == 1 && (M == 3 || M >= 6)) ? 2 : 1;
+  static constexpr int RS = (CLS == 1 && M == 3) ? 2 : 1;
 };
 // Class 1: N > 2048.  From M = 6 those rows take four rows per lane: at M = 8
 // the staged activation tile (about 84 KiB) leaves room for one block per CU,

@@ -155,11 +155,17 @@ def test_decode_projections_and_verify_batches(orc, name):
 # (4200, 4672) and (4500, 7680): one row group per row, walked in several
 # K-tiles (two full tiles and a ragged tail; three full tiles: the
 # double-buffered walk); (16400, 576) and (16390, 2560): N >= 16384, where the
-# rows per lane and the tile length change with M; (1003, 6208): a K-split row
-# whose blocks hold two row sets from M = 2, with a ragged last block
+# rows per lane and the tile length change with M (16390 rows at two rows per
+# lane: 512 blocks of 32 rows and a 6-row tail block); (1003, 6208): a K-split
+# row whose blocks hold two row sets at M = 3, with a ragged last block, and
+# whose one-chunk tiles are walked with the next tile in flight from M = 2;
+# (1000, 4096) and (77, 8256): the same walk in the shorter K-split class;
+# (2049, 5120) and (2600, 6208): K-split grids past one round over the CUs at
+# two rows per lane, ending in one-row-per-lane blocks (a 1-row and a 4-row
+# tail)
 RAGGED = [(8, 64), (10, 192), (37, 576), (300, 2112), (4097, 640), (5000, 320), (4096, 2560), (61, 2560), (300, 5120),
           (2049, 5120), (4200, 4672), (4500, 7680), (16400, 576), (16390, 2560), (1003, 6208), (1000, 4096),
-          (77, 8256)]
+          (77, 8256), (2600, 6208)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)
@@ -573,7 +579,7 @@ def run_mm_g(dw, x_bits, N, group, f32=False):
 # one case per schedule class: tiny, one-chunk K-split, long-row K-split (two
 # row sets from M = 2), one row group per row, several K-tiles (double
 # buffered at M = 1), N >= 16384 with K % 2560 == 0
-G128 = [(8, 128), (300, 2560), (3001, 2560), (1003, 6272), (4097, 768), (4200, 5120), (16400, 2560)]
+G128 = [(8, 128), (300, 2560), (3001, 2560), (1003, 6272), (2300, 6272), (4097, 768), (4200, 5120), (16400, 2560)]
 
 
 @pytest.mark.parametrize("N,K", G128)

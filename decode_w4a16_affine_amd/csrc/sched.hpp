@@ -37,10 +37,9 @@ inline int ksplit_for(int N, int K) {
 // the activation tile of a 5-chunk K-tile alone (M * 10 KiB per block) would
 // cap the CU at two blocks, so those rows take 2-chunk tiles.
 // KSPLIT 4 class 1: long rows (K > 4096), where a whole row fits one K-tile
-// at M = 1; a block may hold two row sets (eight waves, eight row groups) that
-// share one staged activation tile, which halves the activation traffic per
-// row (see Sched<M, 4, CLS> for where that pays).
-// RS: row sets per block (K-split only).
+// at M = 1 (see Sched<M, 4, CLS> for M >= 2).
+// RS: row sets per block (K-split only): a block may hold several row sets
+// that share one staged activation tile; no schedule uses more than one now.
 // KSPLIT 5: one chunk per lane; two rows per lane from M = 2 (in the grouped
 // q/k/v launch, one row per lane doubles the blocks and cost 1.2-2 us per
 // launch at M = 2..5); class 1 (N > 2048) takes four from M = 6.
@@ -64,26 +63,23 @@ struct Sched<M, 1, CLS> {
   static constexpr int DEPTH = (R == 2 && M == 1) ? 3 : 2;
   static constexpr int RS = 1;
 };
-// Long rows (class 1): one row per lane up to M = 5, two from M = 6; two row
-// sets per block only at M = 3 (same-box A/B on the down
-// projection 2560 <- 10240 with the padded staging, us: M = 2 8.61 -> 8.45,
-// M = 3 10.70 -> 10.28, M = 4 14.25 -> 12.53, M = 5 15.46 -> 14.91, M = 8
-// unchanged; the block count 2560 / (4 R RS) then fills all 256 CUs).  From
-// M = 2 the rows walk one-chunk tiles with the next tile in flight
-// (paired_tiles; same-box A/B, us: M = 2 8.51 -> 8.21 with one-chunk instead
-// of two-chunk tiles, M = 4 12.56 -> 12.27, M = 5 14.92 -> 14.40, M = 7
-// 20.4 -> 18.5, M = 8 20.96 -> 20.61; at M = 3 one-chunk tiles were slower,
-// 10.3 -> 11.5, and two rows per lane at M = 4, 5 too, 12.27 -> 12.67).  From
-// M = 6 one row set per block: 320 blocks, which the split grid turns into 256
-// of 8 rows and 128 of 4 (two row sets gave 160 blocks for 256 CUs; same-box
-// A/B, us: M = 6 16.5 -> 14.0, M = 7 18.5 -> 15.9, M = 8 20.6 -> 17.5).
+// Long rows (class 1, the down projection 2560 <- 10240): from M = 2 two rows
+// per lane, one row set per block and one-chunk tiles walked with the next
+// tile in flight (paired_tiles).  Its 320 blocks of 8 rows then run as 256 of
+// 8 rows and 128 of 4 (the split grid of qmm_dense_split_kernel), so no CU
+// holds more than 12 rows and two thirds of them read each activation once
+// for two rows.  Same-box A/B, us, against one row per lane (640 blocks of 4
+// rows): M = 2 8.14 -> 7.50, M = 3 10.26 -> 9.17 (two row sets of two-chunk
+// tiles before), M = 4 12.14 -> 10.82, M = 5 14.42 -> 12.49; from M = 6
+// against two row sets per block (160 blocks for 256 CUs): M = 6 16.5 -> 14.0,
+// M = 8 20.6 -> 17.5.
 template <int M, int CLS>
 struct Sched<M, 4, CLS> {
-  static constexpr int R = (CLS == 1 && M >= 6) ? 2 : 1;
-  static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 && !(CLS == 1 && M == 2) ? 2 : 1);
+  static constexpr int R = (CLS == 1 && M >= 2) ? 2 : 1;
+  static constexpr int CPL = M == 1 ? (CLS == 1 ? 5 : 2) : (M <= 3 && CLS != 1 ? 2 : 1);
   static constexpr int PRE = 1;
   static constexpr int DEPTH = 2;
-  static constexpr int RS = (CLS == 1 && M == 3) ? 2 : 1;
+  static constexpr int RS = 1;
 };
 // Class 1: N > 2048.  From M = 6 those rows take four rows per lane: at M = 8
 // the staged activation tile (about 84 KiB) leaves room for one block per CU,

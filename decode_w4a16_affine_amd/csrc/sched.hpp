@@ -32,7 +32,10 @@ inline int ksplit_for(int N, int K) {
 // of 2560 but not of 2048, so tiles of 5 chunks per lane cover K exactly
 // (otherwise 4); bit 2: tall matrices (N >= 16384), where two rows per lane
 // win once M >= 2 (the activation reads from LDS, 4M bytes per weight and lane,
-// halve; with N >= 16384 the grid still holds 8 waves per CU).  Tiles that
+// halve; with N >= 16384 the grid still holds 8 waves per CU; a grid that is
+// not a whole number of rounds over the CUs ends in one-row-per-lane blocks,
+// see qmm_dense_split_kernel: gate+up 20480 <- 2560 at M = 2 / 3 9.61 -> 9.13
+// and 11.48 -> 10.97 us against one row per lane, same box).  Tiles that
 // cover K exactly use straight-line loads with immediate offsets.  For M >= 6
 // the activation tile of a 5-chunk K-tile alone (M * 10 KiB per block) would
 // cap the CU at two blocks, so those rows take 2-chunk tiles.
@@ -53,7 +56,7 @@ struct Sched;
 template <int M, int CLS>
 struct Sched<M, 1, CLS> {
   static constexpr bool kHead = (CLS & 1) != 0, k2560 = (CLS & 2) != 0, kTall = (CLS & 4) != 0;
-  static constexpr int R = M == 1 ? (kHead ? 2 : 1) : !kTall ? 1 : (k2560 && M <= 3 && !kHead) ? 1 : 2;
+  static constexpr int R = M == 1 ? (kHead ? 2 : 1) : !kTall ? 1 : 2;
   static constexpr int CPL = !kTall || M == 1 ? (k2560 ? 5 : 4)
                              : !k2560 ? 4
                              : M <= 3 ? 5

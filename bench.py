@@ -35,10 +35,17 @@ import synthetic  # noqa: E402
 METRIC = "achieved HBM GB/s (% of MI355X peak) for W4A16 qmv M=1 and qmm M=k+1"
 PEAK_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
-# fp32 fma rate without packed instructions (256 CUs x 4 SIMDs x 16 lanes x 2
-# flops x 2.4 GHz; the packed form that doubles it is not used by the build,
-# and a probe measured 4.25 cycles per wave64 fma per SIMD at that clock).
-PEAK_FP32_FMA_TFLOPS = 78.6
+# MI355X fp32 vector peak (256 CUs x 4 SIMDs x 32 lanes x 2 flops x 2.4 GHz):
+# a wave64 v_fmac_f32 with register operands issues in two cycles per SIMD
+# (measured: 2.3), without the packed instructions the build does not use.
+PEAK_FP32_FMA_TFLOPS = 157.3
+# Issue cycles per wave64 instruction per SIMD by class, at the rate the SIMD
+# executes it: fp32 fma and simple integer ops 2 (32 lanes per cycle), the
+# mixed-precision v_fma_mix_f32 that dequantizes each weight 4 (16 lanes per
+# cycle; measured 2.3 and 4.2 with two or more waves per SIMD).  A packed word
+# (eight weights) costs 8 v_fma_mix_f32, 5 mask/shift ops and 8 M fmas.
+CUS, SIMDS, CLOCK_GHZ = 256, 4, 2.4   # compute units, SIMDs per CU, shader clock
+WORD_ISSUE_CYCLES = (8 * 4 + 5 * 2, 8 * 2)    # (per word, per word and activation row)
 PREFILL_M = (16, 64, 512, 4096)
 LAYERS = 42
 # untimed replay time before each measurement (beyond the warm-up count): the
@@ -57,9 +64,6 @@ def step_bytes(M: int, layers: int) -> int:
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "qmm_dense_decode_step_traffic.json")
-
-
-CUS = 256   # compute units of MI355X
 
 
 def launch_grid(kernel: str, Ns) -> int:
@@ -153,6 +157,19 @@ def unit_flops(M: int, ps) -> int:
 def step_fp32_floor_ms(M: int, layers: int) -> float:
     """The step's fp32 fmas at PEAK_FP32_FMA_TFLOPS (no launch or memory time)."""
     return layers * sum(unit_flops(M, ps) for _, ps in UNITS_GROUPED) / (PEAK_FP32_FMA_TFLOPS * 1e12) * 1e3
+
+
+def unit_issue_floor_us(M: int, ps) -> float:
+    """VALU issue time of the literal arithmetic of one launch spread evenly
+    over every SIMD (WORD_ISSUE_CYCLES per packed word; no launch, memory,
+    LDS or reduction time)."""
+    words = sum(synthetic.PROJECTIONS[p][0] * synthetic.PROJECTIONS[p][1] for p in ps) / 8
+    cycles = words / 64 / (CUS * SIMDS) * (WORD_ISSUE_CYCLES[0] + WORD_ISSUE_CYCLES[1] * M)
+    return cycles / (CLOCK_GHZ * 1e3)
+
+
+def step_issue_floor_ms(M: int, layers: int) -> float:
+    return layers * sum(unit_issue_floor_us(M, ps) for _, ps in UNITS_GROUPED) * 1e-3
 
 
 def capture(torch, fn):
@@ -615,6 +632,7 @@ def main():
                                    fp32_tflops=round(unit_flops(M, unit_ps[u]) / (v * 1e-6) / 1e12, 2),
                                    frac_of_fp32_fma_peak=round(unit_flops(M, unit_ps[u]) / (v * 1e-6) / 1e12
                                                                / PEAK_FP32_FMA_TFLOPS, 4),
+                                   issue_floor_us=round(unit_issue_floor_us(M, unit_ps[u]), 3),
                                    kernel=w4.w4a16_schedule_name(M, *synthetic.PROJECTIONS[unit_ps[u][0]]))
                            for u, v in d.items()}
         log(f"M={M} launches (us): " + ", ".join(f"{u} {v['us']}" for u, v in verify_units[M].items()))
@@ -675,6 +693,7 @@ def main():
                                 fp32_fma_floor_ms=round(step_fp32_floor_ms(M, L), 5),
                                 hbm_floor_ms=round(r["bytes"] / (PEAK_GBS * 1e9) * 1e3, 5),
                                 frac_of_fp32_fma_peak=round(step_fp32_floor_ms(M, L) / r["ms"], 4),
+                                issue_floor_ms=round(step_issue_floor_ms(M, L), 5),
                                 per_launch=verify_units.get(M))
                    for M, r in results.items() if M != 1},
         "roofline": roofline,

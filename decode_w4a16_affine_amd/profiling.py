@@ -228,8 +228,11 @@ def traffic_per_launch(record_path: str, kernel: str, grid_sizes_weights: dict):
 
 
 # VALU issue time of a launch if every SIMD issued one wave64 instruction per
-# 4 cycles (16 lanes per cycle, the rate a probe measured for fp32 fma) at
-# 2.4 GHz: total VALU instructions / (256 CUs x 4 SIMDs) x 4 cycles.
+# 4 cycles at 2.4 GHz: total VALU instructions / (256 CUs x 4 SIMDs) x 4
+# cycles.  4 cycles is the rate of the dequantizing v_fma_mix_f32; fp32 fmas
+# and simple integer ops issue in about 2.3 (two or more waves per SIMD), so
+# for the decode kernels' mix (about 8 of every 53 instructions at M = 5, 8 of
+# 21 at M = 1) this is an upper estimate, roughly 1.3-1.6 times the issue time.
 VALU_US_PER_INSTR = 4.0 / (256 * 4) / 2400.0
 
 
@@ -237,7 +240,7 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
     """Per kernel and grid size: median shader-sequencer counts per launch and
     per wave (VALU and LDS instructions, LDS bank-conflict cycles per LDS
     instruction, wave cycles), and the launch's VALU issue time at one wave
-    instruction per SIMD per 4 cycles."""
+    instruction per SIMD per 4 cycles (an upper estimate, see VALU_US_PER_INSTR)."""
     groups = {}
     for path in csv_path.split(","):   # several counter passes of the same program
         for r in csv.DictReader(open(path)):

@@ -266,6 +266,19 @@ __device__ __forceinline__ void x_stage_tile(const uint4 (&xv)[M][XL], int xq, f
     }
 }
 
+// K-split rows with one row set per block (NT = 64 KSPLIT threads): thread
+// 64 w + l stages pieces 64 w + l + jj NT of a full tile (x_stage_tile), i.e.
+// piece pair 2 (l & 3) of chunk 16 w + l / 4 + jj LPR, and lane t of wave w
+// reads chunks 16 w + t + j LPR: every wave reads only pieces it staged
+// itself.  A walk over several such tiles therefore needs no block barrier
+// around the staging: a wave's LDS operations complete in issue order, and
+// the empty asm with a memory clobber keeps the compiler from moving LDS
+// accesses across it.
+template <int M, int KSPLIT, int RS>
+constexpr bool kWaveX = KSPLIT > 1 && RS == 1;
+
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
 // One K-tile [k0, k0 + klen) of the R rows of this lane's row group.
 // FULL: klen equals the tile size, so every chunk slot of every lane is in
 // range and all offsets are compile-time steps from one base per row (they
@@ -489,9 +502,13 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 // with the next tile's weights in flight: two register sets hold the chunk
 // slots of tiles t and t + 1; consuming slot j of tile t issues slot j of tile
 // t + 2 into the same registers, so between CPL and 2 CPL slots per lane are
-// always in flight, also across the staging barriers.  The next tile's
-// activations are loaded into registers during the current tile and written
-// into the one LDS buffer between two barriers.  Loads past the last tile use
+// always in flight, also across the staging.  The next tile's activations are
+// loaded into registers during the current tile and written into the one LDS
+// buffer, between two barriers, or with one row set per block (kWaveX, where
+// each wave stages what it reads) with no barrier (same-box A/B on the down projection,
+// us: M = 2 7.52 -> 7.03, M = 3 9.19 -> 8.49, M = 5 12.48 -> 11.22; the same
+// for the single-tile walks of the five-way split was faster at M = 2, 3 but
+// slower at M = 1 and 5, q/k/v at M = 5 6.87 -> 8.30).  Loads past the last tile use
 // an out-of-range offset (no traffic, no branch around the load).  Each lane
 // consumes its chunks in the same order with the same body as tile_pass: the
 // sums are bitwise those of the tile-by-tile walk.  xs holds one tile
@@ -508,6 +525,7 @@ __device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>&
   constexpr int PS = kPieceStride<CS, PAD>;
   const int L = w.L;
 
+  static_assert(!kWaveX<M, KSPLIT, RS> || XQ == XL * NT, "whole tiles: every thread stages XL pieces");
   uint4 xv[M][XL];
   auto x_issue = [&](int t) {
     const int tt = min(t, ntiles - 1);
@@ -518,6 +536,12 @@ __device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>&
         const int i = min((int)threadIdx.x + j * NT, XQ - 1);
         xv[m][j] = reinterpret_cast<const uint4*>(xr.p[m] + tt * KTILE)[i];
       }
+  };
+  auto sync = [&]() {
+    if constexpr (kWaveX<M, KSPLIT, RS>)
+      lds_order();
+    else
+      __syncthreads();
   };
 
   // byte offsets of chunk slot 0 of the tile each register set loads next
@@ -548,9 +572,9 @@ __device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>&
     }
   };
   auto stage = [&]() {
-    __syncthreads();   // every wave is done reading the current tile
+    sync();   // every wave that reads the current tile's pieces is done with them
     x_stage_tile<M, XL, NT, PS>(xv, XQ, xs);
-    __syncthreads();
+    sync();
   };
 
   Tile<CPL, R> ta, tb;
@@ -558,13 +582,13 @@ __device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>&
 #pragma unroll
   for (int j = 0; j < CPL; ++j) load(ta, qa, ga, j, true);
   advance2(qa, ga);
-  __syncthreads();   // the block is done with any earlier contents of xs
+  __syncthreads();   // the block is done with any earlier contents of xs and of the K-split sums
   x_stage_tile<M, XL, NT, PS>(xv, XQ, xs);
   x_issue(1);
 #pragma unroll
   for (int j = 0; j < CPL; ++j) load(tb, qb, gb, j, true);
   advance2(qb, gb);
-  __syncthreads();
+  sync();
 
   int t = 0;
   for (; t + 2 <= ntiles; t += 2) {

@@ -150,8 +150,12 @@ struct Tile {
 
 // One 16-byte chunk (32 codes) of R rows against M activation rows.  xc points
 // at the chunk's staged activations: piece p (k = 4p .. 4p+3 of the chunk) of
-// activation row m is xc[(m * 8 + p) * PS].
-template <int M, int R, int PS, bool FAST>
+// activation row m is xc[(m * 8 + p) * PS].  ILV: read a word's activations of
+// every row first and step the R * M accumulators together, one code at a
+// time (independent fmas between two that share an accumulator); otherwise
+// row by row.  Each accumulator sees the same products in the same order
+// either way.
+template <int M, int R, int PS, bool FAST, bool ILV = false>
 __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R], const float (&s)[R],
                                           const float (&b)[R], const float4* xc) {
   float s24[R], s20[R];
@@ -174,15 +178,32 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
       else
         dequant8_plain(word, s[r], b[r], q[r]);
     }
+    if constexpr (ILV) {
+      float xv[M][8];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float4 lo = xc[(m * 8 + 2 * wd) * PS];
-      const float4 hi = xc[(m * 8 + 2 * wd + 1) * PS];
-      const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      for (int m = 0; m < M; ++m) {
+        const float4 lo = xc[(m * 8 + 2 * wd) * PS];
+        const float4 hi = xc[(m * 8 + 2 * wd + 1) * PS];
+        xv[m][0] = lo.x, xv[m][1] = lo.y, xv[m][2] = lo.z, xv[m][3] = lo.w;
+        xv[m][4] = hi.x, xv[m][5] = hi.y, xv[m][6] = hi.z, xv[m][7] = hi.w;
+      }
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[r][m] = __builtin_fmaf(xv[i], q[r][i], acc[r][m]);
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r][m] = __builtin_fmaf(xv[m][i], q[r][i], acc[r][m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float4 lo = xc[(m * 8 + 2 * wd) * PS];
+        const float4 hi = xc[(m * 8 + 2 * wd + 1) * PS];
+        const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[r][m] = __builtin_fmaf(xv[i], q[r][i], acc[r][m]);
+      }
     }
   }
 }
@@ -190,7 +211,7 @@ __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R
 // Chunk slot j of a tile against the staged activations at xc: the bf16
 // scale and bias become fp32 (exact), and the wave takes the plain dequant path
 // for the chunk if any of its lanes holds a scale too large for the fast one.
-template <int M, int R, int PS, int CPL>
+template <int M, int R, int PS, int CPL, bool ILV = false>
 __device__ __forceinline__ void consume_slot(float (&acc)[R][M], const Tile<CPL, R>& tl, int j,
                                              const float4* xc) {
   float s[R], b[R];
@@ -202,9 +223,9 @@ __device__ __forceinline__ void consume_slot(float (&acc)[R][M], const Tile<CPL,
     plain |= needs_plain(s[r]);
   }
   if (__any(plain))
-    chunk_fma<M, R, PS, false>(acc, tl.w[j], s, b, xc);
+    chunk_fma<M, R, PS, false, ILV>(acc, tl.w[j], s, b, xc);
   else
-    chunk_fma<M, R, PS, true>(acc, tl.w[j], s, b, xc);
+    chunk_fma<M, R, PS, true, ILV>(acc, tl.w[j], s, b, xc);
 }
 
 // Per-wave view of the rows being streamed: buffer resources that end at the
@@ -508,7 +529,11 @@ __device__ __forceinline__ void rolled_tiles(float (&acc)[R][M], const XRows<M>&
 // each wave stages what it reads) with no barrier (same-box A/B on the down projection,
 // us: M = 2 7.52 -> 7.03, M = 3 9.19 -> 8.49, M = 5 12.48 -> 11.22; the same
 // for the single-tile walks of the five-way split was faster at M = 2, 3 but
-// slower at M = 1 and 5, q/k/v at M = 5 6.87 -> 8.30).  Loads past the last tile use
+// slower at M = 1 and 5, q/k/v at M = 5 6.87 -> 8.30).  The chunk bodies step
+// all R * M accumulators together (chunk_fma's ILV; same-box A/B on the down
+// projection, us: M = 4 9.86 -> 9.60, M = 5 11.41 -> 11.01, M = 8 16.25 ->
+// 15.17; in the other walks it was slower: o at M = 3 4.42 -> 5.60, the
+// 16384-square at M = 8 86.3 -> 91.4).  Loads past the last tile use
 // an out-of-range offset (no traffic, no branch around the load).  Each lane
 // consumes its chunks in the same order with the same body as tile_pass: the
 // sums are bitwise those of the tile-by-tile walk.  xs holds one tile
@@ -595,7 +620,7 @@ __device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>&
     const bool live_a = t + 2 < ntiles, live_b = t + 3 < ntiles;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      consume_slot<M, R, PS>(acc, ta, j, xs + L + j * LPR);
+      consume_slot<M, R, PS, CPL, true>(acc, ta, j, xs + L + j * LPR);
       load(ta, qa, ga, j, live_a);
     }
     advance2(qa, ga);
@@ -603,7 +628,7 @@ __device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>&
     x_issue(t + 2);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      consume_slot<M, R, PS>(acc, tb, j, xs + L + j * LPR);
+      consume_slot<M, R, PS, CPL, true>(acc, tb, j, xs + L + j * LPR);
       load(tb, qb, gb, j, live_b);
     }
     advance2(qb, gb);
@@ -612,7 +637,7 @@ __device__ __forceinline__ void paired_tiles(float (&acc)[R][M], const XRows<M>&
   }
   if (t < ntiles) {           // an odd count: the last tile is in ta, staged
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) consume_slot<M, R, PS>(acc, ta, j, xs + L + j * LPR);
+    for (int j = 0; j < CPL; ++j) consume_slot<M, R, PS, CPL, true>(acc, ta, j, xs + L + j * LPR);
   }
 }
 

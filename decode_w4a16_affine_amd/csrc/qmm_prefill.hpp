@@ -22,9 +22,12 @@
 // fragment is one 16-byte load of an activation row.
 //
 // A wave owns TM x TN tiles of 16 x 16 outputs (TM * 16 activation rows,
-// TN * 16 weight rows) and walks K in steps of 32.  Rows past M or N are
+// TN * 16 weight rows) and walks K in blocks of four steps of 32 (see
+// PrefillBlock for which codes a lane supplies at which step).  Rows past M or N are
 // clamped on load (so every load is in bounds) and never stored.
 #pragma once
+
+#include <type_traits>
 
 #include "qmm_device.hpp"
 
@@ -53,20 +56,29 @@ __device__ __forceinline__ void split_bf16(const float (&d)[8], bf16x8_t& hi, bf
 
 constexpr int kPrefillWaves = 4;
 
-// One K step (32 codes) of a lane's operands: TM activation fragments, and the
-// packed word and group scale/bias of each of TN weight rows.
+// One block of four K steps (128 codes, 16 packed words per row) of a lane's
+// operands.  The matrix instruction sums its 32 k in an order of its own, so
+// which 8 codes a lane supplies at which step is free as long as both operands
+// agree: lane group lk (lane / 16) supplies words 16 blk + 4 lk + i at step i,
+// so it reads 16 contiguous bytes of each weight row per block (one load, and
+// 64 contiguous bytes per row for the four lane groups) and 64 contiguous
+// bytes of each activation row; the four words share one quantization group
+// (G = 64: words 8g .. 8g + 7; G = 128: 16g .. 16g + 15), so one scale and one
+// bias per row and block.
 template <int TM, int TN>
-struct PrefillStep {
-  bf16x8_t a[TM];
-  uint32_t w[TN];
+struct PrefillBlock {
+  bf16x8_t a[TM][4];
+  uint4 w[TN];
   uint16_t s[TN], b[TN];
 };
 
 // Block of four waves.  KW = 1: the waves own four neighbouring column slabs;
-// KW = 4: the four waves own the same output tile and take every fourth K
-// step, and their partial sums are added in wave order through LDS (for
+// KW = 4: the four waves own the same output tile and take every fourth block
+// of K, and their partial sums are added in wave order through LDS (for
 // problems too small to fill the GPU otherwise).  Each wave keeps the loads of
-// its next two K steps in flight while it computes the current one.
+// its next block in flight while it computes the current one.  A last block of
+// 64 codes (K an odd multiple of 64) leaves lane groups 2 and 3 without codes:
+// they load in-bounds words and multiply zero operands.
 template <int TM, int TN, int KW, int G>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
@@ -77,36 +89,41 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int wn = KW > 1 ? 0 : wave;     // column slab of this wave
-  const int wk = KW > 1 ? wave : 0;     // first K step of this wave
+  const int wk = KW > 1 ? wave : 0;     // first K block of this wave
   const int li = lane & 15;             // row within a 16-row tile
-  const int lk = lane >> 4;             // which 8 of the 32 k of a step
+  const int lk = lane >> 4;             // lane group: words 4 lk .. 4 lk + 3 of a block
   const int m0 = (int)blockIdx.y * (16 * TM);
   const int n0 = ((int)blockIdx.x * kColWaves + wn) * (16 * TN);
-  const uint32_t wpr = (uint32_t)K >> 3, gpr = (uint32_t)K / G;
-  const int steps = K >> 5;
+  const int nw = K >> 3;                // packed words per row (a multiple of 8)
+  const uint32_t gpr = (uint32_t)K / G;
+  const int nblk = (nw + 15) >> 4;
 
   const uint16_t* xr[TM];
 #pragma unroll
-  for (int t = 0; t < TM; ++t) xr[t] = x + (size_t)min(m0 + 16 * t + li, M - 1) * K + 8 * lk;
+  for (int t = 0; t < TM; ++t) xr[t] = x + (size_t)min(m0 + 16 * t + li, M - 1) * K;
   const uint32_t* wr[TN];
   const uint16_t* sr[TN];
   const uint16_t* br[TN];
 #pragma unroll
   for (int u = 0; u < TN; ++u) {
     const size_t n = (size_t)min(n0 + 16 * u + li, N - 1);
-    wr[u] = qw + n * wpr + lk;
+    wr[u] = qw + n * (size_t)nw;
     sr[u] = scales + n * gpr;
     br[u] = biases + n * gpr;
   }
-  // step indices past the last are clamped to it (in-bounds loads, unused)
-  auto load = [&](int st, PrefillStep<TM, TN>& o) {
-    const int k0 = min(st, steps - 1) << 5;
-    const uint32_t g = (uint32_t)(k0 + 8 * lk) / G;
+  // this lane's first word of block blk, clamped in bounds (blocks past the
+  // last repeat it; the half of a 64-code last block past K reads words 4 before)
+  auto first_word = [&](int blk) { return min(16 * min(blk, nblk - 1) + 4 * lk, nw - 4); };
+  auto load = [&](int blk, PrefillBlock<TM, TN>& o) {
+    const int w0 = first_word(blk);
+    const int g = w0 * 8 / G;
 #pragma unroll
-    for (int t = 0; t < TM; ++t) o.a[t] = *reinterpret_cast<const bf16x8_t*>(xr[t] + k0);
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o.a[t][i] = *reinterpret_cast<const bf16x8_t*>(xr[t] + 8 * (w0 + i));
 #pragma unroll
     for (int u = 0; u < TN; ++u) {
-      o.w[u] = wr[u][k0 >> 3];
+      o.w[u] = *reinterpret_cast<const uint4*>(wr[u] + w0);
       o.s[u] = sr[u][g];
       o.b[u] = br[u][g];
     }
@@ -118,20 +135,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
 #pragma unroll
     for (int u = 0; u < TN; ++u) acc[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // A ring of PD steps of operands, PD - 1 steps of loads in flight, named at
-  // compile time (the loop is unrolled by PD), so nothing is copied at the back
-  // edge: a carried operand set that was copied from the freshly loaded one
-  // made the compiler wait for all loads at the end of every step
-  // (vmcnt(0), 0.4 loads outstanding on average).  Same-box A/B against that
-  // loop (us, per-wave form): down 2560 <- 10240 M = 32 / 64 / 128 / 256 81.9 /
-  // 99.6 / 98.8 / 179 -> 80.3 / 95.7 / 93.8 / 177, gate+up M = 24 48.5 -> 45.7;
-  // four or six steps in flight were no faster.  The plain or fast
-  // dequantization is chosen per wave (both give the same bits).
-  constexpr int PD = 3;
-  PrefillStep<TM, TN> buf[PD];
-#pragma unroll
-  for (int i = 0; i < PD - 1; ++i) load(wk + i * KW, buf[i]);
-  auto compute = [&](const PrefillStep<TM, TN>& c) {
+  // The plain or fast dequantization is chosen per wave and block (both give
+  // the same bits).  HALF: the 64-code last block, whose lane groups 2 and 3
+  // feed zero for both operands, so no value of theirs enters a sum.
+  auto compute = [&](const PrefillBlock<TM, TN>& c, auto half_c) {
+    constexpr bool HALF = decltype(half_c)::value;
+    const bool live = !HALF || lk < 2;
     float sv[TN], bv[TN];
     bool plain = false;
 #pragma unroll
@@ -141,34 +150,53 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
       plain |= needs_plain(sv[u]);
     }
     const bool any_plain = __any(plain);
+    const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
-    for (int u = 0; u < TN; ++u) {
-      float d[8];
-      if (any_plain)
-        dequant8_plain(c.w[u], sv[u], bv[u], d);
-      else
-        dequant8_fast(c.w[u], sv[u] * 0x1p24f, sv[u] * 0x1p20f, bv[u], d);
-      bf16x8_t hi, lo;
-      split_bf16(d, hi, lo);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.a[t], hi, acc[t][u], 0, 0, 0);
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.a[t], lo, acc[t][u], 0, 0, 0);
+      for (int u = 0; u < TN; ++u) {
+        const uint32_t word = i == 0 ? c.w[u].x : i == 1 ? c.w[u].y : i == 2 ? c.w[u].z : c.w[u].w;
+        float d[8];
+        if (any_plain)
+          dequant8_plain(word, sv[u], bv[u], d);
+        else
+          dequant8_fast(word, sv[u] * 0x1p24f, sv[u] * 0x1p20f, bv[u], d);
+        bf16x8_t hi, lo;
+        split_bf16(d, hi, lo);
+        if (HALF && !live) hi = lo = zero;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          const bf16x8_t a = (HALF && !live) ? zero : c.a[t][i];
+          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc[t][u], 0, 0, 0);
+          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc[t][u], 0, 0, 0);
+        }
       }
-    }
   };
-  int st = wk;
-  for (; st + (PD - 1) * KW < steps; st += PD * KW) {
-#pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      load(st + (j + PD - 1) * KW, buf[(j + PD - 1) % PD]);
-      compute(buf[j]);
-    }
+  auto compute_block = [&](const PrefillBlock<TM, TN>& c, int blk) {
+    if (16 * blk + 16 <= nw)
+      compute(c, std::false_type{});
+    else
+      compute(c, std::true_type{});
+  };
+  // Two blocks of operands, one block of loads in flight: the next block's
+  // loads go out before the current block is computed (the scheduling
+  // barriers keep the compiler from hoisting the next block's first uses
+  // above its own loads, which turned the wait for the oldest block into a
+  // wait for most of the newest).
+  PrefillBlock<TM, TN> buf0, buf1;
+  int bl = wk;
+  load(bl, buf0);
+  for (; bl + KW < nblk; bl += 2 * KW) {
+    load(bl + KW, buf1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_block(buf0, bl);
+    __builtin_amdgcn_sched_barrier(0);
+    load(bl + 2 * KW, buf0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_block(buf1, bl + KW);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // the last steps (fewer than PD): their loads are already in flight
-#pragma unroll
-  for (int j = 0; j < PD - 1; ++j)
-    if (st + j * KW < steps) compute(buf[j]);
+  if (bl < nblk) compute_block(buf0, bl);
 
   if (KW > 1) {
     // waves 1..KW-1 hand their partial sums to wave 0, which adds them in order

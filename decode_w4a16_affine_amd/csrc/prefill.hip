@@ -15,17 +15,19 @@ namespace w4k {
 
 hipError_t prefill_large(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
                          void* y, int f32, int M, int N, int K, int group, hipStream_t s) {
-  // LDS-tiled form (128 x 128 output tiles, rows past M clamped) for M >= 32:
+  // LDS-tiled form (128 x 128 output tiles, rows past M clamped) for M > 64:
   // with >= 256 tiles one group of four waves per tile; with 64..255 tiles
   // (too few blocks for the CUs) two groups splitting K; fewer tiles, or
-  // M < 32, take the per-wave form below (gate+up 20480 <- 2560, us, per-wave
-  // / tiled: M = 16 45 / 48, M = 32 52 / 48, M = 64 64 / 48, M = 127 145 / 48).
+  // M <= 64 (where a per-wave tile of up to 64 rows reads each weight once),
+  // take the per-wave form below (same box, us, per-wave / tiled: gate+up
+  // 20480 <- 2560 M = 32 31.8 / 45.0, M = 64 43.4 / 47.0, M = 128 102 / 48;
+  // down 2560 <- 10240 M = 512 157 / 164, M = 1024 393 / 165).
   // Measured on MI355X (us, down projection 2560 <- 10240; one group / two
   // groups / per-wave form): M = 256 (40 tiles) 236 / 190 / 181, M = 512 (80)
   // 237 / 191 / 269, M = 1024 (160) 237 / 192 / 700.  256-row tiles of eight
   // waves were 20-50% slower than 128-row tiles of four.
   const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM;
-  if (M >= 32 && tm * tn >= 64) {
+  if (M > 64 && tm * tn >= 64) {
     if (tm * tn > 0x7FFFFFFFL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(tm * tn));
     const bool split = tm * tn < 256;

@@ -650,21 +650,23 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
 
 # ragged M, N and K, both group sizes, tiles and tails in every dimension.  Up
 # to 16 rows (M = 1, 9 below) run the decode kernels on chunks of eight.  The
-# LDS-tiled form (128 x 128 tiles) runs where M >= 32 and there are >= 64
+# LDS-tiled form (128 x 128 tiles) runs where M > 64 and there are >= 64
 # tiles: with >= 256 tiles one group of waves per tile (300 x 12837,
 # 520 x 16390, 256 x 32768 whose grid is permuted across the XCDs, and
 # 100 x 32768 with one partial row tile), with 64..255 tiles two groups
 # splitting K (257 x 4097, 520 x 2560, 300 x 3000 at G = 128, 200 x 8000 with
-# an odd number of K steps, and 40 x 9000 with one partial row tile); the
-# other shapes run the per-wave form (31 x 9000 and 20 x 2560 <- 10240: long
-# K walks with three steps of loads in flight) in 64 x 32 tiles, or in 32 x 16
-# tiles (33 x 300, 100 x 1000, 70 x 513, 64 x 128, 20 x 2560) or 32 x 32 tiles
-# (90 x 2600, ragged in both) where those keep the grid within one block per CU.
+# an odd number of K steps, and 100 x 9000 with one partial row tile); the
+# other shapes run the per-wave form, which walks K in blocks of 128 codes:
+# 64 x 32 tiles (31 x 9000, 40 x 9000 and 20 x 2560 <- 10240: long K walks),
+# 32 x 16 tiles (33 x 300, 100 x 1000, 70 x 513, 64 x 128, 20 x 2560), 32 x 32
+# tiles (90 x 2600, 48 x 3000, ragged in both), 64 x 32 tiles without a
+# K-split (40 x 40000, over 1024 tiles), and a last block of 64 codes
+# (K = 64, 1344, 320).
 PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 4097, 1024, 64), (64, 128, 64, 64),
            (70, 513, 1280, 128), (1, 77, 256, 128), (520, 2560, 2560, 64), (300, 12837, 640, 128),
            (520, 16390, 512, 64), (256, 32768, 256, 64), (300, 3000, 640, 128), (200, 8000, 704, 64),
            (40, 9000, 640, 64), (100, 32768, 256, 128), (31, 9000, 2560, 64), (20, 2560, 10240, 64),
-           (90, 2600, 1024, 128)]
+           (90, 2600, 1024, 128), (100, 9000, 640, 64), (48, 3000, 1344, 64), (40, 40000, 320, 64)]
 
 
 @pytest.mark.parametrize("M,N,K,G", PREFILL)
@@ -752,7 +754,7 @@ def test_prefill_cancelling_rows_within_the_documented_bounds(orc, M, N, K):
     w.scales[cancel] = s_pow2
     w.biases[cancel] = b_neg
     x = synthetic.activations(M, K, seed=M + 9)
-    tiled = M >= 32
+    tiled = M > 64
     say(f"prefill cancelling rows M={M} N={N} K={K} ({'tiled' if tiled else 'per-wave'} form)")
     y32 = run_prefill(DevWeights(w), x, N, f32=True)
     y64, absy = oracle_qmm(orc, x, w, rows=cancel.astype(np.int32))

@@ -154,7 +154,13 @@ struct Tile {
 // every row first and step the R * M accumulators together, one code at a
 // time (independent fmas between two that share an accumulator); otherwise
 // row by row.  Each accumulator sees the same products in the same order
-// either way.
+// either way.  Used by the paired-tile walk and, for one row per lane without
+// a K-split (whose row-by-row order puts every fma right after the one it
+// depends on), by the single-tile walk from M = 2 (same-box A/B on the
+// one-row tail blocks of gate+up 20480 <- 2560, us: M = 3 11.18 -> 10.73,
+// M = 4 12.73 -> 12.37, M = 5 14.28 -> 13.98).  It was slower with two rows
+// per lane as well, in the multi-tile walk of the 16384-square, and in the
+// one-row tail of the five-way split (o at M = 5 5.65 -> 6.80).
 template <int M, int R, int PS, bool FAST, bool ILV = false>
 __device__ __forceinline__ void chunk_fma(float (&acc)[R][M], const uint4 (&w)[R], const float (&s)[R],
                                           const float (&b)[R], const float4* xc) {
@@ -401,9 +407,9 @@ __device__ __forceinline__ void tile_pass(float (&acc)[R][M], const XRows<M>& xr
         plain |= needs_plain(s[r]);
       }
       if (__any(plain))
-        chunk_fma<M, R, PS, false>(acc, tl.w[j], s, b, xs + c);
+        chunk_fma<M, R, PS, false, (KSPLIT == 1 && R == 1 && M >= 2)>(acc, tl.w[j], s, b, xs + c);
       else
-        chunk_fma<M, R, PS, true>(acc, tl.w[j], s, b, xs + c);
+        chunk_fma<M, R, PS, true, (KSPLIT == 1 && R == 1 && M >= 2)>(acc, tl.w[j], s, b, xs + c);
     }
   }
 }

@@ -29,9 +29,12 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-# (object name, source, extra defines)
+# (object name, source, extra arguments)
 UNITS = [(f"inst_m{m}", "inst.hip", [f"-DW4K_M={m}"]) for m in range(1, 9)] + [
-    ("prefill", "prefill.hip", []),
+    # matrix-core results in ordinary VGPRs: by default the compiler gives the
+    # tiled prefill kernel's products to the accumulation registers and reads
+    # every one back before its scaling fma (80 extra VALU per wave and step)
+    ("prefill", "prefill.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("abi", "w4a16.hip", []),
 ]
 

@@ -32,9 +32,10 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+# the device code's sources and the script that holds its compile flags
 KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in
                   ("qmm_device.hpp", "qmm_prefill.hpp", "sched.hpp", "kernels.hpp", "ops.hpp", "inst.hip",
-                   "prefill.hip", "w4a16.hip")]
+                   "prefill.hip", "w4a16.hip")] + [os.path.join(HERE, "build.py")]
 PROBE_LIB = os.path.join(HERE, "libw4a16_probe.so")
 
 
@@ -65,7 +66,7 @@ COPY_BYTES = 256 << 20
 
 
 def kernel_source_sha() -> str:
-    """Hash of the device code; counters taken on other code are stale."""
+    """Hash of the device code and its build flags; counters taken on other code are stale."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(p, "rb") as f:

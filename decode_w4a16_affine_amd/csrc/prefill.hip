@@ -1,5 +1,5 @@
 // Prefill-shaped product above 16 activation rows: the LDS-tiled matrix-core
-// form (qmm_prefill_tiled_kernel) for grids of at least 64 output tiles, the
+// form (qmm_prefill_tiled_kernel) for grids of at least 96 output tiles, the
 // per-wave form (qmm_prefill_kernel) otherwise.  The kernels are in
 // qmm_prefill.hpp; the entry point and the chunked small-M path in w4a16.hip.
 #include <hip/hip_runtime.h>
@@ -16,18 +16,20 @@ namespace w4k {
 hipError_t prefill_large(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
                          void* y, int f32, int M, int N, int K, int group, hipStream_t s) {
   // LDS-tiled form (128 x 128 output tiles, rows past M clamped) for M > 64:
-  // with >= 256 tiles one group of four waves per tile; with 64..255 tiles
+  // with >= 256 tiles one group of four waves per tile; with 96..255 tiles
   // (too few blocks for the CUs) two groups splitting K; fewer tiles, or
   // M <= 64 (where a per-wave tile of up to 64 rows reads each weight once),
   // take the per-wave form below (same box, us, per-wave / tiled: gate+up
   // 20480 <- 2560 M = 32 31.8 / 45.0, M = 64 43.4 / 47.0, M = 128 102 / 48;
-  // down 2560 <- 10240 M = 512 157 / 164, M = 1024 393 / 165).
+  // down 2560 <- 10240 M = 512 (80 tiles) 157.1 / 163.9, M = 640 (100 tiles)
+  // 205.7 / 164.1, M = 1024 393 / 165; 2560 <- 2560 M = 512 41.0 / 44.3,
+  // M = 768 (120 tiles) 52.6 / 45.2).
   // Measured on MI355X (us, down projection 2560 <- 10240; one group / two
   // groups / per-wave form): M = 256 (40 tiles) 236 / 190 / 181, M = 512 (80)
   // 237 / 191 / 269, M = 1024 (160) 237 / 192 / 700.  256-row tiles of eight
   // waves were 20-50% slower than 128-row tiles of four.
   const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM;
-  if (M > 64 && tm * tn >= 64) {
+  if (M > 64 && tm * tn >= 96) {
     if (tm * tn > 0x7FFFFFFFL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(tm * tn));
     const bool split = tm * tn < 256;

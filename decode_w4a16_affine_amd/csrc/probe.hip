@@ -1,7 +1,9 @@
-// Measurement kernels (include/w4a16_probe.h): a plain 128-bit streaming read.
+// Measurement kernels (include/w4a16_probe.h): a plain 128-bit streaming read,
+// and an exhaustive check of the hardware bf16 conversion.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qmm_device.hpp"
 #include "w4a16_probe.h"
 
 namespace {
@@ -31,7 +33,43 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
   if (acc == kNever) sink[0] = acc;
 }
 
+// Every fp32 bit pattern u = 64 (block * 256 + thread) + j, j < 64 (the grid of
+// 2^18 blocks covers all 2^32): the hardware conversion (v_cvt_pk_bf16_f32,
+// what `(__bf16)f` compiles to on gfx950) against the integer
+// round-to-nearest-even helper of the product kernels.  Threads that saw a
+// difference add their count and offer their smallest pattern.
+constexpr int kCvtPerThread = 64;
+constexpr unsigned kCvtBlocks = 1u << 18;
+static_assert((unsigned long long)kCvtBlocks * kThreads * kCvtPerThread == 1ull << 32, "covers every pattern");
+__global__ __launch_bounds__(kThreads) void bf16_round_check_kernel(unsigned long long* __restrict__ mismatches,
+                                                                    uint32_t* __restrict__ first) {
+  const uint32_t base = ((uint32_t)blockIdx.x * kThreads + threadIdx.x) * (uint32_t)kCvtPerThread;
+  unsigned long long n = 0;
+  uint32_t lowest = 0xFFFFFFFFu;
+  for (int j = 0; j < kCvtPerThread; ++j) {
+    const uint32_t u = base + (uint32_t)j;
+    const float f = __uint_as_float(u);
+    const uint32_t hw = __builtin_bit_cast(uint16_t, (__bf16)f);
+    if (hw != w4k::f32_to_bf16(f)) {
+      ++n;
+      lowest = min(lowest, u);
+    }
+  }
+  if (n) {
+    atomicAdd(mismatches, n);
+    atomicMin(first, lowest);
+  }
+}
+
 }  // namespace
+
+extern "C" int w4a16_probe_bf16_round_check(unsigned long long* mismatches, uint32_t* first, void* stream) {
+  if (!mismatches || !first || ((uintptr_t)mismatches % 8) != 0 || ((uintptr_t)first % 4) != 0)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(bf16_round_check_kernel, dim3(kCvtBlocks), dim3(kThreads), 0, (hipStream_t)stream, mismatches,
+                     first);
+  return (int)hipGetLastError();
+}
 
 extern "C" int w4a16_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, int nontemporal,
                                        void* stream) {

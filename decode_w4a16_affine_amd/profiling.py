@@ -39,27 +39,60 @@ KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in
 PROBE_LIB = os.path.join(HERE, "libw4a16_probe.so")
 
 
+PROBE_EXPORTS = ("w4a16_probe_stream_read", "w4a16_probe_bf16_round_check")
+
+
+def probe_lib():
+    """libw4a16_probe.so (include/w4a16_probe.h), loaded once."""
+    import ctypes
+
+    global _probe
+    try:
+        return _probe
+    except NameError:
+        pass
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.w4a16_probe_stream_read.restype = ctypes.c_int
+    lib.w4a16_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p]
+    lib.w4a16_probe_bf16_round_check.restype = ctypes.c_int
+    lib.w4a16_probe_bf16_round_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    _probe = lib
+    return lib
+
+
+def bf16_round_check(torch):
+    """(patterns where the hardware bf16 conversion and the rounding helper
+    differ, the smallest such fp32 pattern or 0xFFFFFFFF): one launch over all
+    2^32 fp32 bit patterns (include/w4a16_probe.h)."""
+    import ctypes
+
+    lib = probe_lib()
+    mism = torch.zeros(1, dtype=torch.int64, device="cuda")
+    first = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = lib.w4a16_probe_bf16_round_check(ctypes.c_void_p(mism.data_ptr()), ctypes.c_void_p(first.data_ptr()),
+                                          ctypes.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError(f"w4a16_probe_bf16_round_check failed: hipError {rc}")
+    torch.cuda.synchronize()
+    return int(mism.item()), int(first.item()) & 0xFFFFFFFF
+
+
 def stream_read(torch, src, sink, blocks: int = 0, nontemporal: bool = True, stream=None) -> None:
     """One launch of the 128-bit streaming-read kernel (include/w4a16_probe.h) over
     the bytes of the contiguous device tensor `src`; `sink` a 4-byte device tensor."""
     import ctypes
 
-    global _probe
-    try:
-        _probe
-    except NameError:
-        if not os.path.exists(PROBE_LIB):
-            raise RuntimeError(f"{PROBE_LIB} is missing: build it with __graft_entry__.build()")
-        _probe = ctypes.CDLL(PROBE_LIB)
-        _probe.w4a16_probe_stream_read.restype = ctypes.c_int
-        _probe.w4a16_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                                   ctypes.c_int, ctypes.c_void_p]
+    lib = probe_lib()
     if not (src.is_cuda and src.is_contiguous() and sink.is_cuda):
         raise ValueError("stream_read takes contiguous device tensors")
     nbytes = src.numel() * src.element_size()
     st = (stream or torch.cuda.current_stream()).cuda_stream
-    rc = _probe.w4a16_probe_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
-                                        blocks, int(bool(nontemporal)), ctypes.c_void_p(st))
+    rc = lib.w4a16_probe_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                     blocks, int(bool(nontemporal)), ctypes.c_void_p(st))
     if rc != 0:
         raise RuntimeError(f"w4a16_probe_stream_read failed: hipError {rc}")
 COPY_BYTES = 256 << 20

@@ -4,7 +4,8 @@
  * them to measure what the hardware gives a plain streaming read, the
  * ceiling every weight-streaming kernel is judged against beside the 8 TB/s
  * HBM specification (tiny-llm W4 page, "Revisit the Decode Roofline": decode
- * time is the streamed bytes over the memory bandwidth).
+ * time is the streamed bytes over the memory bandwidth); a test uses the
+ * second to check a hardware conversion one product kernel relies on.
  */
 #ifndef W4A16_PROBE_H
 #define W4A16_PROBE_H
@@ -31,6 +32,21 @@ extern "C" {
  */
 int w4a16_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks, int nontemporal,
                             void *stream);
+
+/*
+ * Converts every one of the 2^32 fp32 bit patterns to bf16 twice, with the
+ * hardware's packed conversion (v_cvt_pk_bf16_f32, which the LDS-tiled
+ * prefill epilogue uses) and with the integer round-to-nearest-even rule
+ * the other kernels use (NaNs quieted, sign and payload top bits kept), and
+ * adds the number of patterns where the two differ to *mismatches (device
+ * memory, 8-byte aligned; the caller sets it to 0) and lowers *first (device
+ * memory, 4-byte aligned; the caller sets it to 0xFFFFFFFF) to the smallest
+ * such pattern.  One launch of 2^18 workgroups on `stream`; the results are
+ * there once the stream has run it.
+ * Returns 0, or a nonzero hipError_t value if a pointer is NULL or
+ * misaligned or the launch failed.
+ */
+int w4a16_probe_bf16_round_check(unsigned long long *mismatches, uint32_t *first, void *stream);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,23 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+def test_every_declared_probe_symbol_is_exported():
+    # the measurement library (include/w4a16_probe.h) the benchmark and the
+    # conversion test load
+    from decode_w4a16_affine_amd import profiling
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "w4a16_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(w4a16_probe_[a-z0-9_]+)\s*\(", text)))
+    assert set(names) == set(profiling.PROBE_EXPORTS)
+    P = profiling.probe_lib()
+    for n in names:
+        assert hasattr(P, n), n
+    # invalid arguments are refused before any launch
+    assert P.w4a16_probe_bf16_round_check(None, A16, None) != 0
+    assert P.w4a16_probe_bf16_round_check(A4, A16, None) != 0
+    assert P.w4a16_probe_stream_read(None, 16, A16, 0, 1, None) != 0
+    assert P.w4a16_probe_stream_read(A16, 15, A16, 0, 1, None) != 0
+
+
 def test_abi_version_and_status_strings(L):
     assert w4.w4a16_abi_version() == 2
     seen = set()

@@ -286,8 +286,8 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
     lines = ["# Shader-sequencer counters per launch", "", f"Command: `{command}`", "",
              "| kernel | grid | waves | VALU instr / wave | VALU issue (us, all SIMDs) | LDS instr / wave | "
              "LDS conflict cycles / LDS instr | "
-             "wave cycles / wave |" + (" MFMA instr / wave | MFMA busy / CU busy (per SIMD) | waiting on a dependency "
-                                       "/ wave cycles | waiting on LDS / wave cycles |" if matrix else ""),
+             "wave cycles / wave |" + (" MFMA instr / wave | MFMA busy / CU busy (per SIMD) | SQ_WAIT_INST_ANY "
+                                       "/ wave cycles | SQ_WAIT_INST_LDS / wave cycles |" if matrix else ""),
              "|---|---|---|---|---|---|---|---|" + ("---|---|---|---|" if matrix else "")]
     for (k, g), d in sorted(groups.items()):
         med = {c: statistics.median(v) for c, v in d.items()}
@@ -308,7 +308,7 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
     # every cycle, so divided by the wave cycles it is the average in flight)
     extra = [(k, g, d) for (k, g), d in sorted(groups.items()) if "SQ_WAIT_ANY" in d and "SQ_INST_LEVEL_VMEM" in d]
     if extra:
-        lines += ["", "| kernel | grid | waiting (any) / wave cycles | vector-memory reads / wave | "
+        lines += ["", "| kernel | grid | SQ_WAIT_ANY / wave cycles | vector-memory reads / wave | "
                       "vector-memory instructions in flight (average) |", "|---|---|---|---|---|"]
         for k, g, d in extra:
             med = {c: statistics.median(v) for c, v in d.items()}
@@ -316,6 +316,24 @@ def summarize_sq(csv_path: str, out_md: str, command: str) -> None:
             waves = med.get("SQ_WAVES", 0.0) or 1.0
             lines.append(f"| `{k}` | {g} | {med['SQ_WAIT_ANY'] / wc:.2f} | "
                          f"{med.get('SQ_INSTS_VMEM_RD', 0.0) / waves:.0f} | {med['SQ_INST_LEVEL_VMEM'] / wc:.2f} |")
+    # wave states, where a pass collected them: SQ_WAIT_ANY (wave-cycles spent
+    # waiting for anything), SQ_WAIT_INST_ANY (waiting for any instruction
+    # issue) and SQ_ACTIVE_INST_ANY (working on instructions), each over the
+    # wave cycles; the three add up to about one
+    states = [(k, g, d) for (k, g), d in sorted(groups.items())
+              if all(c in d for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY"))]
+    if states:
+        lines += ["", "Wave states, fractions of SQ_WAVE_CYCLES:", "",
+                  "| kernel | grid | waves | SQ_WAIT_ANY | SQ_WAIT_INST_ANY | SQ_ACTIVE_INST_ANY | "
+                  "SQ_ACTIVE_INST_VALU | SQ_ACTIVE_INST_LDS | vector-memory instructions in flight (average) |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for k, g, d in states:
+            med = {c: statistics.median(v) for c, v in d.items()}
+            wc = max(med.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+            cell = lambda c: f"{med[c] / wc:.2f}" if c in med else "-"   # noqa: E731
+            lines.append(f"| `{k}` | {g} | {int(med.get('SQ_WAVES', 0.0))} | {cell('SQ_WAIT_ANY')} | "
+                         f"{cell('SQ_WAIT_INST_ANY')} | {cell('SQ_ACTIVE_INST_ANY')} | {cell('SQ_ACTIVE_INST_VALU')} | "
+                         f"{cell('SQ_ACTIVE_INST_LDS')} | {cell('SQ_INST_LEVEL_VMEM')} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 

@@ -6,6 +6,7 @@ profiles/qmm_dense_decode_step_traffic.md); bench.launch_grid must reproduce
 them from the kernel name and the matrix heights, including the split grids
 whose blocks after the last whole round over the CUs hold one row per lane.
 """
+import csv
 import os
 import subprocess
 import sys
@@ -63,3 +64,35 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_counter_summary_tables(tmp_path):
+    # one kernel, two dispatches per counter (the summary takes the median);
+    # a non-library kernel in the same file is left out
+    from decode_w4a16_affine_amd import profiling
+    name = "void w4k::qmm_dense_kernel<5, 2, 1, 5, 1, 1, 1, 64>(int)"
+    counters = {"SQ_WAVES": 320, "SQ_WAVE_CYCLES": 1000, "SQ_INSTS_VALU": 6400, "SQ_INSTS_LDS": 640,
+                "SQ_LDS_BANK_CONFLICT": 320, "SQ_WAIT_ANY": 250, "SQ_WAIT_INST_ANY": 350, "SQ_ACTIVE_INST_ANY": 400,
+                "SQ_ACTIVE_INST_VALU": 300, "SQ_INST_LEVEL_VMEM": 120}
+    path = tmp_path / "c.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for dispatch in range(2):
+            for c, v in counters.items():
+                w.writerow([20480, name, c, v * (1 + dispatch)])   # medians: 1.5 x
+            w.writerow([256, "void other_kernel()", "SQ_WAVES", 1])
+    out = tmp_path / "c.md"
+    profiling.summarize_sq(str(path), str(out), "cmd")
+    text = out.read_text()
+    assert "other_kernel" not in text
+    rows = [l for l in text.splitlines() if l.startswith("| `qmm_dense_kernel<5, 2, 1, 5, 1, 1, 1, 64>`")]
+    assert len(rows) == 3   # instructions, memory waits, wave states
+    first = [c.strip() for c in rows[0].split("|")[1:-1]]
+    # waves 480, VALU / wave 20, LDS / wave 2, conflict cycles / LDS instr 0.5, wave cycles / wave 3.125 -> 3
+    assert first[1:4] == ["20480", "480", "20"] and first[5:8] == ["2", "0.50", "3"]
+    # SQ_WAIT_ANY / wave cycles, vector-memory reads / wave (not collected), loads in flight
+    assert [c.strip() for c in rows[1].split("|")[1:-1]][2:] == ["0.25", "0", "0.12"]
+    states = [c.strip() for c in rows[2].split("|")[1:-1]]
+    # fractions of SQ_WAVE_CYCLES; no SQ_ACTIVE_INST_LDS was collected
+    assert states[3:9] == ["0.25", "0.35", "0.40", "0.30", "-", "0.12"]

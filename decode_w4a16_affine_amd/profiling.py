@@ -108,8 +108,8 @@ def kernel_source_sha() -> str:
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(qmm_\w+_kernel<[^>]*>|argmax_finalize_kernel|dequant_rows_kernel|gather_rows_kernel|pack_kernel)",
-                  name)
+    m = re.search(r"(qmm_\w+_kernel<[^>]*>|argmax_finalize_kernel|dequant_rows_kernel|gather_rows_kernel|pack_kernel|"
+                  r"stream_read_kernel|bf16_round_check_kernel)", name)
     return m.group(1) if m else name.split("(")[0][:80]
 
 

@@ -1,6 +1,7 @@
 // Prefill-shaped product above 16 activation rows: the LDS-tiled matrix-core
-// form (qmm_prefill_tiled_kernel) for grids of at least 96 output tiles, the
-// per-wave form (qmm_prefill_kernel) otherwise.  The kernels are in
+// form (qmm_prefill_tiled_kernel) for grids of at least 96 output tiles of
+// 128 rows or 160 of 64 rows, the per-wave form (qmm_prefill_kernel)
+// otherwise.  The kernels are in
 // qmm_prefill.hpp; the entry point and the chunked small-M path in w4a16.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,18 +29,31 @@ hipError_t prefill_large(const uint16_t* x, const uint32_t* qw, const uint16_t* 
   // groups / per-wave form): M = 256 (40 tiles) 236 / 190 / 181, M = 512 (80)
   // 237 / 191 / 269, M = 1024 (160) 237 / 192 / 700.  256-row tiles of eight
   // waves were 20-50% slower than 128-row tiles of four.
-  const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM;
-  if (M > 64 && tm * tn >= 96) {
-    if (tm * tn > 0x7FFFFFFFL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(tm * tn));
-    const bool split = tm * tn < 256;
+  // Tiles of 64 rows (two waves of 32 rows, 118 registers, so four waves per
+  // SIMD) where 128-row tiles are too few for one group per tile and 64-row
+  // tiles number 160..255 (two K groups each).  Same box, us, 128-row tiles
+  // or per-wave form -> 64-row tiles: down 2560 <- 10240 M = 512 (160 tiles)
+  // 158.1 -> 117.7, M = 768 (240) 164.3 -> 117.3; 2560 <- 2560 M = 512 41.2 ->
+  // 31.7, M = 768 45.2 -> 32.0.  Slower elsewhere: 120 tiles (down M = 384
+  // 107.9 per-wave -> 117.3) and from 256 tiles, one K group each (down
+  // M = 1024 165.2 -> 186.1, gate+up M = 128 47.5 -> 54.5).
+  const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM, tm64 = (M + 63) / 64;
+  const bool half_rows = M > 64 && tm * tn < 256 && tm64 * tn >= 160 && tm64 * tn < 256;
+  if (half_rows || (M > 64 && tm * tn >= 96)) {
+    const long tiles = half_rows ? tm64 * tn : tm * tn;
+    if (tiles > 0x7FFFFFFFL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles);
+    const bool split = tiles < 256;
     auto go = [&](auto kernel, int threads) {
       hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, x, qw, scales, biases, y, M, N, K, f32, (int)tn);
     };
-    if (group == 128)
-      split ? go(qmm_prefill_tiled_kernel<128, 2>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<128, 1>, kPfThreads);
+    if (half_rows)   // fewer than 256 tiles: always two K groups
+      group == 128 ? go(qmm_prefill_tiled_kernel<128, 2, 2>, 2 * kPfThreads)
+                   : go(qmm_prefill_tiled_kernel<64, 2, 2>, 2 * kPfThreads);
+    else if (group == 128)
+      split ? go(qmm_prefill_tiled_kernel<128, 2, 4>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<128, 1, 4>, kPfThreads);
     else
-      split ? go(qmm_prefill_tiled_kernel<64, 2>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<64, 1>, kPfThreads);
+      split ? go(qmm_prefill_tiled_kernel<64, 2, 4>, 2 * kPfThreads) : go(qmm_prefill_tiled_kernel<64, 1, 4>, kPfThreads);
     return hipGetLastError();
   }
   // Tiles of 64 activation rows x 32 weight rows per wave; when fewer than

@@ -237,7 +237,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void qmm_prefill_kernel(
 
 // ---------------------------------------------------------------------------
 // LDS-tiled form for large M.  A block of four waves owns a 128 x 128 output
-// tile and walks K in steps of 64 codes.  Per step the block stages the
+// tile (or 64 x 128, see qmm_prefill_tiled_kernel) and walks K in steps of 64
+// codes.  Per step the block stages the
 // activation tile (128 rows x 64 bf16), the weight tile as centred codes
 // (128 rows x 64 bf16 integers) and each weight row's scale and shifted bias
 // in LDS; each wave then multiplies a 64 x 64 piece from LDS with the
@@ -262,18 +263,20 @@ __device__ __forceinline__ int prefill_tile_of(int b, int nb) {
 }
 
 // One K step's global operands of a thread (kept as separate values: arrays
-// or structs of them were placed in LDS by the compiler): four 16-byte
+// or structs of them were placed in LDS by the compiler): NA (4 or 2) 16-byte
 // activation pieces, four packed weight words (32 codes of one row), and the
 // group's scale and bias bits.
-template <int G>
+template <int G, int NA>
 __device__ __forceinline__ void pf_load(uint4& a0, uint4& a1, uint4& a2, uint4& a3, uint4& w, uint32_t& s,
                                         uint32_t& b, const uint16_t* x0, const uint16_t* x1, const uint16_t* x2,
                                         const uint16_t* x3, const uint32_t* wq, const uint16_t* ws,
                                         const uint16_t* wb, int k0, int bq) {
   a0 = *reinterpret_cast<const uint4*>(x0 + k0);
   a1 = *reinterpret_cast<const uint4*>(x1 + k0);
-  a2 = *reinterpret_cast<const uint4*>(x2 + k0);
-  a3 = *reinterpret_cast<const uint4*>(x3 + k0);
+  if constexpr (NA == 4) {
+    a2 = *reinterpret_cast<const uint4*>(x2 + k0);
+    a3 = *reinterpret_cast<const uint4*>(x3 + k0);
+  }
   w = *reinterpret_cast<const uint4*>(wq + (k0 >> 3));
   const int g = (k0 + 32 * bq) / G;
   s = ws[g];
@@ -316,14 +319,17 @@ __device__ __forceinline__ uint4 centred_codes8(uint32_t w) {
 }
 
 // activations, centred codes and the row's (s, b + 8 s) of one step into LDS
+template <int NA>
 __device__ __forceinline__ void pf_stage_codes(const uint4& a0, const uint4& a1, const uint4& a2, const uint4& a3,
                                                const uint4& w, uint32_t s, uint32_t b, uint16_t* As, uint16_t* Bq,
                                                float2* sb, int ao0, int ao1, int ao2, int ao3, int boff, int br,
                                                int bq) {
   *reinterpret_cast<uint4*>(As + ao0) = a0;
   *reinterpret_cast<uint4*>(As + ao1) = a1;
-  *reinterpret_cast<uint4*>(As + ao2) = a2;
-  *reinterpret_cast<uint4*>(As + ao3) = a3;
+  if constexpr (NA == 4) {
+    *reinterpret_cast<uint4*>(As + ao2) = a2;
+    *reinterpret_cast<uint4*>(As + ao3) = a3;
+  }
   *reinterpret_cast<uint4*>(Bq + boff) = centred_codes8(w.x);
   *reinterpret_cast<uint4*>(Bq + boff + 8) = centred_codes8(w.y);
   *reinterpret_cast<uint4*>(Bq + boff + 16) = centred_codes8(w.z);
@@ -334,22 +340,23 @@ __device__ __forceinline__ void pf_stage_codes(const uint4& a0, const uint4& a1,
   }
 }
 
-// a wave's 64 x 64 piece of one staged step: X for its four 16-row activation
-// fragments (ones operand), then per 16-row weight tile P over both K halves
-// and the scaled update of the sums
-__device__ __forceinline__ void pf_compute_codes(f32x4_t (&acc)[4][4], const uint16_t* As, const uint16_t* Bq,
+// a wave's (16 TMW) x 64 piece of one staged step: X for its TMW 16-row
+// activation fragments (ones operand), then per 16-row weight tile P over both
+// K halves and the scaled update of the sums
+template <int TMW>
+__device__ __forceinline__ void pf_compute_codes(f32x4_t (&acc)[TMW][4], const uint16_t* As, const uint16_t* Bq,
                                                  const float2* sb, int arow, int brow, int lk) {
-  bf16x8_t a[2][4];
+  bf16x8_t a[2][TMW];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TMW; ++t)
       a[ks][t] = *reinterpret_cast<const bf16x8_t*>(As + (arow + t * 16) * kPfStr + ks * 32 + 8 * lk);
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4_t X[4];
+  f32x4_t X[TMW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < TMW; ++t) {
     X[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][t], ones, zero, 0, 0, 0);
     X[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][t], ones, X[t], 0, 0, 0);
   }
@@ -360,7 +367,7 @@ __device__ __forceinline__ void pf_compute_codes(f32x4_t (&acc)[4][4], const uin
     const bf16x8_t q1 = *reinterpret_cast<const bf16x8_t*>(Bq + o + 32);
     const float2 c = sb[brow + u * 16];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < TMW; ++t) {
       f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][t], q0, zero, 0, 0, 0);
       P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][t], q1, P, 0, 0, 0);
 #pragma unroll
@@ -374,35 +381,40 @@ __device__ __forceinline__ void pf_compute_codes(f32x4_t (&acc)[4][4], const uin
 // group 1 hands its sums to group 0 through LDS, which adds them (group 0's
 // partial first, then group 1's: a fixed order, so results are deterministic).
 // Both groups execute the same barriers, also when the step count is odd.
-template <int G, int KS>
+// TMW: 16-row activation fragments per wave (4: 128 x 128 block tiles, 2:
+// 64 x 128, for grids with few 128-row tiles: half the matrix work per staged
+// code, but twice the blocks and 118 instead of ~190 registers).
+template <int G, int KS, int TMW>
 __global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, void* __restrict__ y, int M, int N, int K, int out_f32, int tiles_n) {
   constexpr int NT = kPfThreads;   // threads per K group
-  constexpr int TILE = kPfBM * kPfStr;
-  static_assert(kPfBN == kPfBM, "activation and weight tiles of one size");
-  static_assert(kPfBN * (kPfBK / 8) == 4 * NT && kPfBM * (kPfBK / 8) == 4 * NT, "four 16-byte pieces per thread");
+  constexpr int BM = 32 * TMW;     // block tile rows (two waves of 16 TMW rows)
+  constexpr int ATILE = BM * kPfStr, BTILE = kPfBN * kPfStr;
+  static_assert(TMW == 4 || TMW == 2, "row fragments per wave");
+  static_assert(kPfBN * (kPfBK / 8) == 4 * NT && BM * (kPfBK / 8) == TMW * NT, "16-byte pieces per thread");
   static_assert(KS == 1 || KS == 2, "K groups");
   // per K group: activation tile, code tile, (s, b') per weight row
-  constexpr int GROUP_LDS = 2 * TILE + 4 * kPfBN;
-  static_assert(KS == 1 || 16 * NT * 16 <= KS * GROUP_LDS * 2, "group sums fit in the tiles");
+  constexpr int GROUP_LDS = ATILE + BTILE + 4 * kPfBN;
+  static_assert(KS == 1 || TMW * 4 * NT * 16 <= KS * GROUP_LDS * 2, "group sums fit in the tiles");
   __shared__ __attribute__((aligned(16))) uint16_t lds[KS * GROUP_LDS];
   const int kg = (int)threadIdx.x / NT;   // K group
   const int tid = (int)threadIdx.x % NT;  // thread within the group
   uint16_t* As = lds + kg * GROUP_LDS;
-  uint16_t* Bq = As + TILE;
-  float2* sb = reinterpret_cast<float2*>(Bq + TILE);
+  uint16_t* Bq = As + ATILE;
+  float2* sb = reinterpret_cast<float2*>(Bq + BTILE);
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int tile = prefill_tile_of((int)blockIdx.x, (int)gridDim.x);
-  const int m0 = tile / tiles_n * kPfBM, n0 = tile % tiles_n * kPfBN;
+  const int m0 = tile / tiles_n * BM, n0 = tile % tiles_n * kPfBN;
 
-  // staging: activation piece p = tid + NT i (row p / 8, 16-byte column p % 8);
-  // weight row tid / 2, words 4 (tid % 2) .. +3 of the step (one 16-byte
-  // load).  Rows past M or N are clamped (in-bounds loads, never stored).
+  // staging: activation piece p = tid + NT i, i < TMW (row p / 8, 16-byte
+  // column p % 8); weight row tid / 2, words 4 (tid % 2) .. +3 of the step
+  // (one 16-byte load).  Rows past M or N are clamped (in-bounds loads, never
+  // stored).  With TMW = 2 the pieces 2 and 3 are neither loaded nor staged.
   auto xrow = [&](int i) { return x + (size_t)min(m0 + (tid + NT * i) / 8, M - 1) * K + 8 * (tid % 8); };
   auto aofs = [&](int i) { return (tid + NT * i) / 8 * kPfStr + 8 * (tid % 8); };
-  const uint16_t *x0 = xrow(0), *x1 = xrow(1), *x2 = xrow(2), *x3 = xrow(3);
-  const int ao0 = aofs(0), ao1 = aofs(1), ao2 = aofs(2), ao3 = aofs(3);
+  const uint16_t *x0 = xrow(0), *x1 = xrow(1), *x2 = TMW == 4 ? xrow(2) : x0, *x3 = TMW == 4 ? xrow(3) : x0;
+  const int ao0 = aofs(0), ao1 = aofs(1), ao2 = TMW == 4 ? aofs(2) : ao0, ao3 = TMW == 4 ? aofs(3) : ao0;
   const int br = tid >> 1, bq = tid & 1;
   const size_t bn = (size_t)min(n0 + br, N - 1);
   const uint32_t* wq = qw + bn * (size_t)(K >> 3) + 4 * bq;
@@ -410,12 +422,12 @@ __global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
   const uint16_t* wb = biases + bn * (size_t)(K / G);
   const int boff = br * kPfStr + 32 * bq;
 
-  const int wm = wave >> 1, wn = wave & 1;   // this wave's 64 x 64 piece
+  const int wm = wave >> 1, wn = wave & 1;   // this wave's (16 TMW) x 64 piece
   const int li = lane & 15, lk = lane >> 4;
-  const int arow = wm * 64 + li, brow = wn * 64 + li;
-  f32x4_t acc[4][4];
+  const int arow = wm * 16 * TMW + li, brow = wn * 64 + li;
+  f32x4_t acc[TMW][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < TMW; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -425,24 +437,24 @@ __global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
   uint4 a0, a1, a2, a3, w;
   uint32_t s, b;
   if constexpr (KS == 1) {
-    pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
+    pf_load<G, TMW>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, 0, bq);
     for (int st = 0; st < steps; ++st) {
       __syncthreads();   // every wave is done reading the previous step's tiles
-      pf_stage_codes(a0, a1, a2, a3, w, s, b, As, Bq, sb, ao0, ao1, ao2, ao3, boff, br, bq);
+      pf_stage_codes<TMW>(a0, a1, a2, a3, w, s, b, As, Bq, sb, ao0, ao1, ao2, ao3, boff, br, bq);
       __syncthreads();
-      if (st + 1 < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
-      pf_compute_codes(acc, As, Bq, sb, arow, brow, lk);
+      if (st + 1 < steps) pf_load<G, TMW>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + 1) * kPfBK, bq);
+      pf_compute_codes<TMW>(acc, As, Bq, sb, arow, brow, lk);
     }
   } else {
     const int iters = (steps + KS - 1) / KS;
-    if (kg < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, kg * kPfBK, bq);
+    if (kg < steps) pf_load<G, TMW>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, kg * kPfBK, bq);
     for (int it = 0; it < iters; ++it) {
       const int st = it * KS + kg;
       __syncthreads();   // every wave is done reading the previous step's tiles
-      if (st < steps) pf_stage_codes(a0, a1, a2, a3, w, s, b, As, Bq, sb, ao0, ao1, ao2, ao3, boff, br, bq);
+      if (st < steps) pf_stage_codes<TMW>(a0, a1, a2, a3, w, s, b, As, Bq, sb, ao0, ao1, ao2, ao3, boff, br, bq);
       __syncthreads();
-      if (st + KS < steps) pf_load<G>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + KS) * kPfBK, bq);
-      if (st < steps) pf_compute_codes(acc, As, Bq, sb, arow, brow, lk);
+      if (st + KS < steps) pf_load<G, TMW>(a0, a1, a2, a3, w, s, b, x0, x1, x2, x3, wq, ws, wb, (st + KS) * kPfBK, bq);
+      if (st < steps) pf_compute_codes<TMW>(acc, As, Bq, sb, arow, brow, lk);
     }
   }
   if constexpr (KS == 2) {
@@ -450,26 +462,26 @@ __global__ __launch_bounds__(kPfThreads * KS) void qmm_prefill_tiled_kernel(
     __syncthreads();   // the tiles are free
     if (kg == 1) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < TMW; ++t)
 #pragma unroll
         for (int u = 0; u < 4; ++u) part[(t * 4 + u) * NT + tid] = acc[t][u];
     }
     __syncthreads();
     if (kg == 1) return;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TMW; ++t)
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc[t][u] += part[(t * 4 + u) * NT + tid];
   }
 
-  // element i of fragment (t, u): row m0 + 64 wm + 16 t + 4 lk + i, column
+  // element i of fragment (t, u): row m0 + 16 TMW wm + 16 t + 4 lk + i, column
   // n0 + 64 wn + 16 u + li (one row offset per (t, i), immediate column
   // steps).  The bf16 conversion is the hardware's (v_cvt_pk_bf16_f32), which
   // gives the bits of f32_to_bf16 for every fp32 pattern (all 2^32 compared
   // on MI355X) in one instruction per two values instead of ~8 per value.
-  const int mr = m0 + wm * 64 + 4 * lk, nc = n0 + wn * 64 + li;
+  const int mr = m0 + wm * 16 * TMW + 4 * lk, nc = n0 + wn * 64 + li;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < TMW; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mr + 16 * t + i;

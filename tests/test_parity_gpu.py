@@ -650,15 +650,16 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
 
 # ragged M, N and K, both group sizes, tiles and tails in every dimension.  Up
 # to 16 rows (M = 1, 9 below) run the decode kernels on chunks of eight.  The
-# LDS-tiled form (128 x 128 tiles) runs where M > 64 and there are >= 96
-# tiles: with >= 256 tiles one group of waves per tile (300 x 12837,
-# 520 x 16390, 256 x 32768 whose grid is permuted across the XCDs, and
-# 100 x 32768 with one partial row tile), with 96..255 tiles two groups
-# splitting K (257 x 4097, 520 x 2560, 300 x 4000 at G = 128, 200 x 8000 with
-# an odd number of K steps, and 100 x 12500 with one partial row tile); the
-# other shapes run the per-wave form, which walks K in blocks of 128 codes
-# (300 x 3000 at G = 128 and 100 x 9000: 72 and 71 tiles, below the tiled
-# form's threshold):
+# LDS-tiled form runs where M > 64 and there are >= 96 tiles of 128 x 128 or
+# 160..255 of 64 x 128: with >= 256 128-row tiles one group of waves per tile
+# (300 x 12837, 520 x 16390, 256 x 32768 whose grid is permuted across the
+# XCDs, and 100 x 32768 with one partial row tile); with 96..255 of them and
+# not 160..255 64-row tiles, two groups splitting K (100 x 20480, and
+# 100 x 24576 at G = 128); with 160..255 64-row tiles, 64-row tiles and two
+# groups (257 x 4097, 520 x 2560, 300 x 4000 at G = 128, 200 x 8000 with an
+# odd number of K steps, and 100 x 12500 with one partial row tile); the other
+# shapes run the per-wave form, which walks K in blocks of 128 codes
+# (300 x 3000 at G = 128 and 100 x 9000: 120 and 142 64-row tiles):
 # 64 x 32 tiles (31 x 9000, 40 x 9000 and 20 x 2560 <- 10240: long K walks),
 # 32 x 16 tiles (33 x 300, 100 x 1000, 70 x 513, 64 x 128, 20 x 2560), 32 x 32
 # tiles (90 x 2600, 48 x 3000, ragged in both), 64 x 32 tiles without a
@@ -669,7 +670,7 @@ PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 40
            (520, 16390, 512, 64), (256, 32768, 256, 64), (300, 3000, 640, 128), (200, 8000, 704, 64),
            (40, 9000, 640, 64), (100, 32768, 256, 128), (31, 9000, 2560, 64), (20, 2560, 10240, 64),
            (90, 2600, 1024, 128), (100, 9000, 640, 64), (48, 3000, 1344, 64), (40, 40000, 320, 64),
-           (300, 4000, 640, 128), (100, 12500, 640, 64)]
+           (300, 4000, 640, 128), (100, 12500, 640, 64), (100, 20480, 640, 64), (100, 24576, 256, 128)]
 
 
 @pytest.mark.parametrize("M,N,K,G", PREFILL)
@@ -708,8 +709,8 @@ def test_prefill_maximum_rows(orc):
 @pytest.mark.parametrize("M,N,K", [(20, 64, 2560), (200, 32768, 256), (150, 8192, 640)])
 def test_prefill_crafted_scales(orc, M, N, K):
     # signs, zero, subnormal and |s| >= 2^100 scales (the plain dequant path),
-    # in the per-wave (M = 20), LDS-tiled (M = 200) and K-split tiled (M = 150,
-    # 128 tiles) forms
+    # in the per-wave (M = 20), LDS-tiled (M = 200) and 64-row tiled (M = 150,
+    # 192 tiles) forms
     w = synthetic.quantized_weights(N, K, seed=41)
     w.scales, w.biases = crafted_scales(N, K // 64, seed=41)
     x = synthetic.activations(M, K, seed=41)
@@ -724,7 +725,7 @@ def test_prefill_crafted_scales(orc, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(100, 1000, 640), (384, 4096, 2560), (1024, 4096, 1280)])
 def test_prefill_zero_weight_rows_exact(orc, M, N, K):
     # rows stored as q = 8, b = -8 s hold w = 0 exactly, so their outputs are
-    # exactly 0 in the per-wave (M = 100), K-split tiled (96 tiles) and tiled
+    # exactly 0 in the per-wave (M = 100), 64-row tiled (192 tiles) and tiled
     # (256 tiles) forms; the other rows stay within the bound
     w = synthetic.quantized_weights(N, K, seed=N + 5, bias="exact")
     zero = np.arange(3, N, 7)
@@ -744,7 +745,7 @@ def test_prefill_cancelling_rows_within_the_documented_bounds(orc, M, N, K):
     # rows whose every code is 15 with b = -15 s (s a power of two, so b is
     # exact in bf16) dequantize to w = 0 exactly: the oracle gives 0 with a
     # bound of 0.  The per-wave form (M = 20) splits each w into bf16 parts and
-    # returns exactly 0.  The LDS-tiled forms (96 and 256 tiles) use the
+    # returns exactly 0.  The LDS-tiled forms (64-row and 128-row tiles) use the
     # rearranged sums s * sum(x (q - 8)) + (b + 8 s) * sum(x), whose rounding is
     # bounded on sum |s x (q - 8)| + |(b + 8 s) x| instead (the documented
     # bound of w4a16_matmul_prefill): their residue must stay within 1e-3 of
@@ -757,7 +758,8 @@ def test_prefill_cancelling_rows_within_the_documented_bounds(orc, M, N, K):
     w.scales[cancel] = s_pow2
     w.biases[cancel] = b_neg
     x = synthetic.activations(M, K, seed=M + 9)
-    tiled = M > 64 and -(-M // 128) * -(-N // 128) >= 96   # the entry point's choice of form
+    t128, t64 = -(-M // 128) * -(-N // 128), -(-M // 64) * -(-N // 128)
+    tiled = M > 64 and (t128 >= 96 or (t128 < 256 and 160 <= t64 < 256))   # the entry point's choice of form
     say(f"prefill cancelling rows M={M} N={N} K={K} ({'tiled' if tiled else 'per-wave'} form)")
     y32 = run_prefill(DevWeights(w), x, N, f32=True)
     y64, absy = oracle_qmm(orc, x, w, rows=cancel.astype(np.int32))

@@ -213,8 +213,9 @@ def w4a16_matmul_prefill(x, qw, scales, biases, y, group: int = GROUP, stream=No
     """y[M,N] = x[M,K] . W^T for prefill-sized M (matrix cores; not bitwise equal to w4a16_matmul).
 
     Up to 16 rows: the decode kernels on chunks of 8 rows (their bound and
-    results).  Small grids: bounded on sum |w x|.  The LDS-tiled form (M > 64,
-    at least 96 output tiles of 128 x 128 or 160 of 64 x 128) uses the rearranged per-group sums
+    results).  Small grids: bounded on sum |w x|.  The LDS-tiled form (M > 64
+    and at least 96 output tiles of 128 x 128, or M > 40 and 160..255 of
+    64 x 128) uses the rearranged per-group sums
     and is bounded on sum |s x (q - 8)| + |(b + 8 s) x|, which is weaker where
     the dequantized weights cancel."""
     M, K = _activations(x)

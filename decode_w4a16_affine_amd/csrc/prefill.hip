@@ -1,7 +1,7 @@
 // Prefill-shaped product above 16 activation rows: the LDS-tiled matrix-core
 // form (qmm_prefill_tiled_kernel) for grids of at least 96 output tiles of
-// 128 rows or 160 of 64 rows, the per-wave form (qmm_prefill_kernel)
-// otherwise.  The kernels are in
+// 128 rows (M > 64) or 160..255 of 64 rows (M > 40), the per-wave form
+// (qmm_prefill_kernel) otherwise.  The kernels are in
 // qmm_prefill.hpp; the entry point and the chunked small-M path in w4a16.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,9 +36,12 @@ hipError_t prefill_large(const uint16_t* x, const uint32_t* qw, const uint16_t* 
   // 158.1 -> 117.7, M = 768 (240) 164.3 -> 117.3; 2560 <- 2560 M = 512 41.2 ->
   // 31.7, M = 768 45.2 -> 32.0.  Slower elsewhere: 120 tiles (down M = 384
   // 107.9 per-wave -> 117.3) and from 256 tiles, one K group each (down
-  // M = 1024 165.2 -> 186.1, gate+up M = 128 47.5 -> 54.5).
+  // M = 1024 165.2 -> 186.1, gate+up M = 128 47.5 -> 54.5).  They also take
+  // M = 41..64 where the grid has 160..255 of them (gate+up, per-wave form ->
+  // 64-row tiles: M = 48 37.5 -> 33.3, M = 64 43.2 -> 33.7; slower at M = 32,
+  // 31.5 -> 33.0, and M = 17, 28.5 -> 32.2).
   const long tn = (N + kPfBN - 1) / kPfBN, tm = (M + kPfBM - 1) / kPfBM, tm64 = (M + 63) / 64;
-  const bool half_rows = M > 64 && tm * tn < 256 && tm64 * tn >= 160 && tm64 * tn < 256;
+  const bool half_rows = M > 40 && tm * tn < 256 && tm64 * tn >= 160 && tm64 * tn < 256;
   if (half_rows || (M > 64 && tm * tn >= 96)) {
     const long tiles = half_rows ? tm64 * tn : tm * tn;
     if (tiles > 0x7FFFFFFFL) return hipErrorInvalidValue;

@@ -650,14 +650,15 @@ def run_prefill(dw, x_bits, N, group=64, f32=False):
 
 # ragged M, N and K, both group sizes, tiles and tails in every dimension.  Up
 # to 16 rows (M = 1, 9 below) run the decode kernels on chunks of eight.  The
-# LDS-tiled form runs where M > 64 and there are >= 96 tiles of 128 x 128 or
-# 160..255 of 64 x 128: with >= 256 128-row tiles one group of waves per tile
+# LDS-tiled form runs where M > 64 and there are >= 96 tiles of 128 x 128, or
+# M > 40 and 160..255 of 64 x 128: with >= 256 128-row tiles one group of waves per tile
 # (300 x 12837, 520 x 16390, 256 x 32768 whose grid is permuted across the
 # XCDs, and 100 x 32768 with one partial row tile); with 96..255 of them and
 # not 160..255 64-row tiles, two groups splitting K (100 x 20480, and
 # 100 x 24576 at G = 128); with 160..255 64-row tiles, 64-row tiles and two
 # groups (257 x 4097, 520 x 2560, 300 x 4000 at G = 128, 200 x 8000 with an
-# odd number of K steps, and 100 x 12500 with one partial row tile); the other
+# odd number of K steps, 100 x 12500 with one partial row tile, and
+# 48 x 20480 and 60 x 24000 at G = 128 with a single partial row tile); the other
 # shapes run the per-wave form, which walks K in blocks of 128 codes
 # (300 x 3000 at G = 128 and 100 x 9000: 120 and 142 64-row tiles):
 # 64 x 32 tiles (31 x 9000, 40 x 9000 and 20 x 2560 <- 10240: long K walks),
@@ -670,7 +671,8 @@ PREFILL = [(9, 40, 128, 64), (33, 300, 640, 64), (100, 1000, 2560, 64), (257, 40
            (520, 16390, 512, 64), (256, 32768, 256, 64), (300, 3000, 640, 128), (200, 8000, 704, 64),
            (40, 9000, 640, 64), (100, 32768, 256, 128), (31, 9000, 2560, 64), (20, 2560, 10240, 64),
            (90, 2600, 1024, 128), (100, 9000, 640, 64), (48, 3000, 1344, 64), (40, 40000, 320, 64),
-           (300, 4000, 640, 128), (100, 12500, 640, 64), (100, 20480, 640, 64), (100, 24576, 256, 128)]
+           (300, 4000, 640, 128), (100, 12500, 640, 64), (100, 20480, 640, 64), (100, 24576, 256, 128),
+           (48, 20480, 2560, 64), (60, 24000, 640, 128)]
 
 
 @pytest.mark.parametrize("M,N,K,G", PREFILL)
@@ -759,7 +761,7 @@ def test_prefill_cancelling_rows_within_the_documented_bounds(orc, M, N, K):
     w.biases[cancel] = b_neg
     x = synthetic.activations(M, K, seed=M + 9)
     t128, t64 = -(-M // 128) * -(-N // 128), -(-M // 64) * -(-N // 128)
-    tiled = M > 64 and (t128 >= 96 or (t128 < 256 and 160 <= t64 < 256))   # the entry point's choice of form
+    tiled = (M > 64 and t128 >= 96) or (M > 40 and t128 < 256 and 160 <= t64 < 256)   # the entry point's choice of form
     say(f"prefill cancelling rows M={M} N={N} K={K} ({'tiled' if tiled else 'per-wave'} form)")
     y32 = run_prefill(DevWeights(w), x, N, f32=True)
     y64, absy = oracle_qmm(orc, x, w, rows=cancel.astype(np.int32))

@@ -159,6 +159,23 @@ def step_fp32_floor_ms(M: int, layers: int) -> float:
     return layers * sum(unit_flops(M, ps) for _, ps in UNITS_GROUPED) / (PEAK_FP32_FMA_TFLOPS * 1e12) * 1e3
 
 
+def prefill_matrix_factor(M: int, N: int):
+    """Matrix-core work of w4a16_matmul_prefill over its algorithmic 2 M N K
+    flops, by the form the entry point picks: 128-row LDS tiles 1.25 (a pass
+    over the codes and a quarter-size pass for the activation sums), 64-row
+    tiles 1.5 (that pass is half the size), the per-wave form 2 (hi and lo
+    weight parts); None up to 16 rows (decode kernels, no matrix cores)."""
+    if M <= 16:
+        return None
+    t128 = -(-M // 128) * -(-N // 128)
+    t64 = -(-M // 64) * -(-N // 128)
+    if M > 40 and t128 < 256 and 160 <= t64 < 256:
+        return 1.5
+    if M > 64 and t128 >= 96:
+        return 1.25
+    return 2.0
+
+
 def unit_issue_floor_us(M: int, ps) -> float:
     """VALU issue time of the literal arithmetic of one launch spread evenly
     over every SIMD (WORD_ISSUE_CYCLES per packed word; no launch, memory,
@@ -425,12 +442,8 @@ def config_timings(torch, w4, reps: int = 5):
 
     # prefill-sized products (w4a16_matmul_prefill, matrix cores) on the decode
     # stack's gate+up and down shapes: flop-bound, so priced against the dense
-    # bf16 matrix-core peak.  Algorithmic flops are 2*M*N*K.  From M = 512
-    # both shapes run the LDS-tiled form, whose matrix cores execute 1.25x that
-    # (a pass over the codes, and a quarter-size pass for the activation sums);
-    # M = 16 runs the decode kernels on two 8-row chunks and M = 64 the tiled
-    # form (gate+up) or the per-wave form (down), so for those two the
-    # matrix-core figure is not reported.
+    # bf16 matrix-core peak.  Algorithmic flops are 2*M*N*K; the matrix cores
+    # execute prefill_matrix_factor(M, N) times that (mfma_tflops).
     out["prefill"] = {}
     for name in ("gate_up", "down"):
         N, K = synthetic.PROJECTIONS[name]
@@ -446,8 +459,9 @@ def config_timings(torch, w4, reps: int = 5):
             r = timed(calls, call_bytes(M, N, K))
             tflops = 2.0 * M * N * K / (r["us"] * 1e-6) / 1e12
             r.update(tflops=round(tflops, 1), frac_of_bf16_peak=round(tflops / PEAK_BF16_TFLOPS, 4))
-            if M >= 512:
-                r.update(mfma_tflops=round(1.25 * tflops, 1))
+            factor = prefill_matrix_factor(M, N)
+            if factor is not None:
+                r.update(mfma_tflops=round(factor * tflops, 1))
             out["prefill"][name][str(M)] = r
             del x, y
         del qw, sc, bi

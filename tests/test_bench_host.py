@@ -96,3 +96,14 @@ def test_counter_summary_tables(tmp_path):
     states = [c.strip() for c in rows[2].split("|")[1:-1]]
     # fractions of SQ_WAVE_CYCLES; no SQ_ACTIVE_INST_LDS was collected
     assert states[3:9] == ["0.25", "0.35", "0.40", "0.30", "-", "0.12"]
+
+
+def test_prefill_matrix_factor_follows_the_dispatch():
+    # gate+up 20480 <- 2560 and down 2560 <- 10240 at the benchmark's M
+    f = bench.prefill_matrix_factor
+    assert f(16, 20480) is None and f(16, 2560) is None       # decode kernels on 8-row chunks
+    assert f(64, 20480) == 1.5                                 # 160 tiles of 64 rows
+    assert f(64, 2560) == 2.0                                  # per-wave form
+    assert f(512, 20480) == 1.25 and f(4096, 20480) == 1.25    # 128-row tiles
+    assert f(512, 2560) == 1.5                                 # 80 tiles of 128 rows, 160 of 64
+    assert f(384, 2560) == 2.0 and f(1024, 2560) == 1.25 and f(4096, 2560) == 1.25

@@ -129,9 +129,9 @@ w4a16_status_t w4a16_matmul_geglu(const uint16_t *x, const uint32_t *qw, const u
  * Up to 16 rows run the decode kernels on chunks of at most 8 rows (each
  * chunk bitwise equal to a w4a16_matmul call on those rows; a launch error
  * on the second chunk leaves the first chunk's rows written).  Larger M with
- * at least 96 output tiles of 128 x 128 (and M > 64), or 160..255 of 64 x 128
- * (and M > 40), use the
- * page's rearranged sums ("Quantized Matrix Multiplication"): per 64 codes,
+ * at least 96 output tiles of 128 x 128 (and M > 64), or 160..255 of
+ * 64 x 128 (and M > 40), use the page's rearranged sums ("Quantized Matrix
+ * Multiplication"): per 64 codes,
  * y += s * sum(x * (q - 8)) + (b + 8 s) * sum(x), the centred codes entering
  * the matrix cores as exact bf16 integers; its rounding is bounded on
  * sum |s x (q - 8)| + |(b + 8 s) x| rather than sum |w x| (close for
